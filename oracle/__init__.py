@@ -1,0 +1,17 @@
+"""CPU oracle (test infrastructure only; see fsdp_oracle's header)."""
+
+from .fsdp_oracle import (  # noqa: F401
+    AdamW,
+    UnitLayout,
+    adamw_scalars,
+    adamw_step,
+    bf16_round_nearest_even,
+    bf16_widen,
+    cast_unflatten,
+    flatten_pad,
+    numel,
+    persistent_bytes,
+    reduce_adamw_shard,
+    reduce_shard,
+    unit_layout,
+)
