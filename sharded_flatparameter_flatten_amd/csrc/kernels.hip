@@ -1,0 +1,665 @@
+// HIP kernels of libfsdpshard.so for CDNA4 (gfx950) and the device entry
+// points of the C ABI (include/fsdp_shard.h).
+//
+// Everything on this path streams through HBM once; nothing is a dense
+// contraction, so there is no MFMA here. The design is about bytes:
+//  * each thread owns 8 consecutive elements, so every bf16 gradient load and
+//    every bf16 store is one 128-bit access and every fp32 state array moves in
+//    two 128-bit accesses; a 64-lane wavefront covers 1 KiB of bf16 per load;
+//  * workgroups of 256 threads own contiguous 2048-element tiles, so every
+//    64-byte line is written whole by one wavefront;
+//  * the fused step reads the n_grads gradient rows, master, m and v once and
+//    writes master, m, v (and the bf16 parameter) once: the fp32 reduced
+//    gradient never touches memory;
+//  * buffers that are not 16-byte aligned (e.g. a rank window r*S with S odd)
+//    take a lane-strided scalar path, still coalesced per instruction;
+//  * the gather/unflatten and flatten/pad copies are planned on the host as
+//    (source, destination, length) segments (tensor x shard intersections),
+//    passed in kernel arguments and walked per workgroup with a scalar cursor.
+//
+// Numerics: every floating-point step is one binary32 operation with round to
+// nearest even. The file is compiled with -ffp-contract=off (and the pragma
+// below) so no multiply-add is fused; division and sqrt use the correctly
+// rounded expansions (the HIP default, never -ffast-math); fp32 denormals are
+// kept.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "fsdp_internal.h"
+
+#pragma clang fp contract(off)
+
+#ifndef FSDP_GRID_CAP
+#define FSDP_GRID_CAP 0   // 0: one workgroup per tile; otherwise a grid-stride cap
+#endif
+
+using fsdp::fail;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;
+constexpr int64_t kTile = int64_t(kThreads) * kVec;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// element numerics
+// ---------------------------------------------------------------------------
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> canonical quiet NaN.
+// Adding 0x7FFF plus the lowest kept bit rounds the dropped half correctly and
+// carries into the exponent (up to infinity) when the kept part overflows.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t x = __float_as_uint(f);
+  if ((x & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (x + 0x7FFFu + ((x >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return to_bf16(a) | (to_bf16(b) << 16);
+}
+
+struct Adam {
+  float gs, b1, omb1, b2, omb2, bc1, bc2, lr, eps, wd;
+};
+
+// One AdamW element (Adam with bias correction, decoupled decay scaled by lr).
+__device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, const Adam& s) {
+  const float m_new = s.b1 * m + s.omb1 * g;
+  const float v_new = s.b2 * v + s.omb2 * (g * g);
+  const float m_hat = m_new / s.bc1;
+  const float v_hat = v_new / s.bc2;
+  const float denom = sqrtf(v_hat) + s.eps;
+  const float u = m_hat / denom;
+  p = p - s.lr * (u + s.wd * p);
+  m = m_new;
+  v = v_new;
+}
+
+// ---------------------------------------------------------------------------
+// memory helpers (128-bit)
+// ---------------------------------------------------------------------------
+
+template <typename V>
+__device__ __forceinline__ V ld(const void* p) {
+  return *reinterpret_cast<const V*>(p);
+}
+template <typename V>
+__device__ __forceinline__ void st(void* p, V x) {
+  *reinterpret_cast<V*>(p) = x;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 q, float (&x)[8]) {
+  x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
+  x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
+  x[4] = lo_bf16(q.z); x[5] = hi_bf16(q.z);
+  x[6] = lo_bf16(q.w); x[7] = hi_bf16(q.w);
+}
+
+__device__ __forceinline__ void accumulate8(u32x4 q, float (&x)[8]) {
+  x[0] = x[0] + lo_bf16(q.x); x[1] = x[1] + hi_bf16(q.x);
+  x[2] = x[2] + lo_bf16(q.y); x[3] = x[3] + hi_bf16(q.y);
+  x[4] = x[4] + lo_bf16(q.z); x[5] = x[5] + hi_bf16(q.z);
+  x[6] = x[6] + lo_bf16(q.w); x[7] = x[7] + hi_bf16(q.w);
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = ld<f32x4>(p), b = ld<f32x4>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  st<f32x4>(p, f32x4{x[0], x[1], x[2], x[3]});
+  st<f32x4>(p + 4, f32x4{x[4], x[5], x[6], x[7]});
+}
+
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const float (&x)[8]) {
+  st<u32x4>(p, u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                     pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])});
+}
+
+// ---------------------------------------------------------------------------
+// reduce / AdamW / fused step kernels
+// ---------------------------------------------------------------------------
+
+struct StepArgs {
+  const uint16_t* g[FSDP_MAX_RANKS];  // rank-window start of each contribution
+  const float* grad;                  // AdamW input (unfused)
+  float* out;                         // reduce output (unfused)
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* w;                        // bf16 parameter out, or null
+  int64_t n;                          // shard_valid
+  int32_t n_grads;
+  int32_t pad_;
+  Adam s;
+};
+
+enum class Op { Reduce, AdamW, Fused };
+
+// Left fold of the gradient rows for 8 consecutive elements at i. NG > 0 is
+// the compile-time count (all loads issued before the first add); NG == 0
+// reads the count at run time and walks the rows in chunks of 8.
+template <int NG>
+__device__ __forceinline__ void reduce8(const StepArgs& a, int64_t i, float (&acc)[8]) {
+  if constexpr (NG > 0) {
+    u32x4 q[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) q[k] = ld<u32x4>(a.g[k] + i);
+    unpack8(q[0], acc);
+#pragma unroll
+    for (int k = 1; k < NG; ++k) accumulate8(q[k], acc);
+  } else {
+    const int ng = a.n_grads;
+    unpack8(ld<u32x4>(a.g[0] + i), acc);
+    int k = 1;
+    for (; k + 8 <= ng; k += 8) {
+      u32x4 q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = ld<u32x4>(a.g[k + j] + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) accumulate8(q[j], acc);
+    }
+    for (; k < ng; ++k) accumulate8(ld<u32x4>(a.g[k] + i), acc);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a.s.gs;
+}
+
+template <Op OP>
+__device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
+  float g;
+  if constexpr (OP == Op::AdamW) {
+    g = a.grad[i];
+  } else {
+    g = widen(a.g[0][i]);
+    for (int k = 1; k < a.n_grads; ++k) g = g + widen(a.g[k][i]);
+    g = g * a.s.gs;
+  }
+  if constexpr (OP == Op::Reduce) {
+    a.out[i] = g;
+  } else {
+    float p = a.p[i], m = a.m[i], v = a.v[i];
+    adamw(g, p, m, v, a.s);
+    a.p[i] = p;
+    a.m[i] = m;
+    a.v[i] = v;
+    if (a.w) a.w[i] = static_cast<uint16_t>(to_bf16(p));
+  }
+}
+
+// Vector path: every buffer 16-byte aligned. Thread t of a tile owns elements
+// [tile + 8t, tile + 8t + 8); the last partial group falls back to scalars.
+template <Op OP, int NG, bool EMIT>
+__global__ __launch_bounds__(kThreads) void k_step_vec(StepArgs a) {
+  const int64_t n = a.n;
+  const int64_t stride = int64_t(gridDim.x) * kTile;
+  for (int64_t i = int64_t(blockIdx.x) * kTile + int64_t(threadIdx.x) * kVec; i < n;
+       i += stride) {
+    if (i + kVec <= n) {
+      float g[8];
+      if constexpr (OP == Op::AdamW) {
+        load8(a.grad + i, g);
+      } else {
+        reduce8<NG>(a, i, g);
+      }
+      if constexpr (OP == Op::Reduce) {
+        store8(a.out + i, g);
+      } else {
+        float p[8], m[8], v[8];
+        load8(a.p + i, p);
+        load8(a.m + i, m);
+        load8(a.v + i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
+        store8(a.p + i, p);
+        store8(a.m + i, m);
+        store8(a.v + i, v);
+        if constexpr (EMIT) store8_bf16(a.w + i, p);
+      }
+    } else {
+      for (int64_t j = i; j < n; ++j) step_scalar<OP>(a, j);
+    }
+  }
+}
+
+// Scalar path for unaligned buffers: element tile + j*256 + t, so each
+// instruction of a wavefront still touches 64 consecutive elements.
+template <Op OP>
+__global__ __launch_bounds__(kThreads) void k_step_scalar(StepArgs a) {
+  const int64_t n = a.n;
+  const int64_t stride = int64_t(gridDim.x) * kTile;
+  for (int64_t base = int64_t(blockIdx.x) * kTile; base < n; base += stride) {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int64_t i = base + int64_t(j) * kThreads + threadIdx.x;
+      if (i < n) step_scalar<OP>(a, i);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// segment copy: flatten/pad and gather/unflatten
+// ---------------------------------------------------------------------------
+
+enum : int32_t { kSegVec = 0, kSegScalar = 1, kSegZeroVec = 2, kSegZeroScalar = 3 };
+
+struct Seg {
+  const void* src;     // null for zero fill
+  void* dst;
+  int64_t len;         // elements
+  int64_t tile_end;    // exclusive prefix of tiles over the batch
+  int32_t mode;
+  int32_t pad_;
+};
+
+constexpr int kMaxSeg = 64;
+
+struct SegArgs {
+  Seg seg[kMaxSeg];
+  int64_t tiles;
+  int32_t nseg;
+  int32_t pad_;
+};
+
+// KIND 0: 4-byte bit copy; 1: 2-byte bit copy; 2: fp32 -> bf16 (nearest even).
+template <int KIND>
+struct CopyKind;
+template <>
+struct CopyKind<0> {
+  using S = uint32_t;
+  using D = uint32_t;
+  static __device__ __forceinline__ D cvt(S x) { return x; }
+};
+template <>
+struct CopyKind<1> {
+  using S = uint16_t;
+  using D = uint16_t;
+  static __device__ __forceinline__ D cvt(S x) { return x; }
+};
+template <>
+struct CopyKind<2> {
+  using S = float;
+  using D = uint16_t;
+  static __device__ __forceinline__ D cvt(S x) { return static_cast<uint16_t>(to_bf16(x)); }
+};
+
+template <int KIND>
+__device__ __forceinline__ void copy8(const void* src, void* dst) {
+  if constexpr (KIND == 0) {
+    st<u32x4>(dst, ld<u32x4>(src));
+    st<u32x4>(static_cast<uint32_t*>(dst) + 4, ld<u32x4>(static_cast<const uint32_t*>(src) + 4));
+  } else if constexpr (KIND == 1) {
+    st<u32x4>(dst, ld<u32x4>(src));
+  } else {
+    float x[8];
+    load8(static_cast<const float*>(src), x);
+    store8_bf16(static_cast<uint16_t*>(dst), x);
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ void zero8(void* dst) {
+  st<u32x4>(dst, u32x4{0u, 0u, 0u, 0u});
+  if constexpr (KIND == 0) st<u32x4>(static_cast<uint32_t*>(dst) + 4, u32x4{0u, 0u, 0u, 0u});
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
+  using K = CopyKind<KIND>;
+  using S = typename K::S;
+  using D = typename K::D;
+  int s = 0;
+  for (int64_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
+    while (t >= a.seg[s].tile_end) ++s;   // workgroup-uniform cursor
+    const int64_t tile0 = s == 0 ? 0 : a.seg[s - 1].tile_end;
+    const int64_t base = (t - tile0) * kTile;
+    const int64_t len = a.seg[s].len;
+    const int32_t mode = a.seg[s].mode;
+    const S* src = static_cast<const S*>(a.seg[s].src);
+    D* dst = static_cast<D*>(a.seg[s].dst);
+    if (mode == kSegVec || mode == kSegZeroVec) {
+      const int64_t i = base + int64_t(threadIdx.x) * kVec;
+      if (i + kVec <= len) {
+        if (mode == kSegVec) copy8<KIND>(src + i, dst + i);
+        else zero8<KIND>(dst + i);
+      } else {
+        for (int64_t j = i; j < len; ++j) dst[j] = mode == kSegVec ? K::cvt(src[j]) : D(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int64_t e = base + int64_t(j) * kThreads + threadIdx.x;
+        if (e < len) dst[e] = mode == kSegScalar ? K::cvt(src[e]) : D(0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch helpers
+// ---------------------------------------------------------------------------
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+unsigned grid_for(int64_t tiles) {
+  int64_t g = tiles;
+  if (FSDP_GRID_CAP > 0 && g > FSDP_GRID_CAP) g = FSDP_GRID_CAP;
+  return static_cast<unsigned>(std::max<int64_t>(g, 1));
+}
+
+fsdp_status after_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(FSDP_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return FSDP_OK;
+}
+
+template <Op OP, bool EMIT>
+void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
+  if constexpr (OP == Op::AdamW) {
+    k_step_vec<OP, 0, EMIT><<<grid, kThreads, 0, stream>>>(a);
+  } else {
+  switch (a.n_grads) {
+#define FSDP_NG_CASE(K) \
+  case K: k_step_vec<OP, K, EMIT><<<grid, kThreads, 0, stream>>>(a); break;
+    FSDP_NG_CASE(1)
+    FSDP_NG_CASE(2)
+    FSDP_NG_CASE(3)
+    FSDP_NG_CASE(4)
+    FSDP_NG_CASE(5)
+    FSDP_NG_CASE(6)
+    FSDP_NG_CASE(7)
+    FSDP_NG_CASE(8)
+    FSDP_NG_CASE(16)
+#undef FSDP_NG_CASE
+    default: k_step_vec<OP, 0, EMIT><<<grid, kThreads, 0, stream>>>(a); break;
+  }
+  }
+}
+
+template <Op OP>
+fsdp_status launch_step(const StepArgs& a, bool vec, hipStream_t stream, const char* what) {
+  if (a.n <= 0) return FSDP_OK;
+  const unsigned grid = grid_for((a.n + kTile - 1) / kTile);
+  if (vec) {
+    if (a.w) launch_vec_ng<OP, true>(a, grid, stream);
+    else launch_vec_ng<OP, false>(a, grid, stream);
+  } else {
+    k_step_scalar<OP><<<grid, kThreads, 0, stream>>>(a);
+  }
+  return after_launch(what);
+}
+
+struct Piece {
+  const void* src;   // null: zero fill
+  void* dst;
+  int64_t len;
+};
+
+// Splits each piece into an unaligned scalar head and a 16-byte aligned vector
+// body when some head length h < 8 aligns both sides; otherwise the whole
+// piece is scalar. Then launches the segments in batches of kMaxSeg.
+fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_t stream,
+                          const char* what) {
+  const int64_t ss = kind == 1 ? 2 : 4;      // source element bytes
+  const int64_t ds = kind == 0 ? 4 : 2;      // destination element bytes
+  std::vector<Seg> segs;
+  segs.reserve(pieces.size() * 2);
+  for (const Piece& pc : pieces) {
+    if (pc.len <= 0) continue;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(pc.src);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(pc.dst);
+    int64_t head = -1;
+    for (int64_t h = 0; h < kVec && h < pc.len; ++h) {
+      const bool s_ok = pc.src == nullptr || ((s0 + h * ss) & 15u) == 0;
+      const bool d_ok = ((d0 + h * ds) & 15u) == 0;
+      if (s_ok && d_ok) { head = h; break; }
+    }
+    const int32_t vmode = pc.src ? kSegVec : kSegZeroVec;
+    const int32_t smode = pc.src ? kSegScalar : kSegZeroScalar;
+    if (head < 0) {
+      segs.push_back(Seg{pc.src, pc.dst, pc.len, 0, smode, 0});
+      continue;
+    }
+    if (head > 0) segs.push_back(Seg{pc.src, pc.dst, head, 0, smode, 0});
+    const void* vs = pc.src ? reinterpret_cast<const void*>(s0 + head * ss) : nullptr;
+    void* vd = reinterpret_cast<void*>(d0 + head * ds);
+    segs.push_back(Seg{vs, vd, pc.len - head, 0, vmode, 0});
+  }
+  for (size_t b = 0; b < segs.size(); b += kMaxSeg) {
+    SegArgs a{};
+    const size_t nb = std::min<size_t>(kMaxSeg, segs.size() - b);
+    int64_t tiles = 0;
+    for (size_t j = 0; j < nb; ++j) {
+      a.seg[j] = segs[b + j];
+      tiles += (a.seg[j].len + kTile - 1) / kTile;
+      a.seg[j].tile_end = tiles;
+    }
+    a.nseg = static_cast<int32_t>(nb);
+    a.tiles = tiles;
+    const unsigned grid = grid_for(tiles);
+    switch (kind) {
+      case 0: k_segcopy<0><<<grid, kThreads, 0, stream>>>(a); break;
+      case 1: k_segcopy<1><<<grid, kThreads, 0, stream>>>(a); break;
+      default: k_segcopy<2><<<grid, kThreads, 0, stream>>>(a); break;
+    }
+    if (fsdp_status st = after_launch(what)) return st;
+  }
+  return FSDP_OK;
+}
+
+Adam to_device(const fsdp::AdamScalars& h) {
+  return Adam{h.gs, h.b1, h.omb1, h.b2, h.omb2, h.bc1, h.bc2, h.lr, h.eps, h.wd};
+}
+
+fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
+                        std::vector<fsdp::ByteRange>* ranges, StepArgs* a) {
+  if (n_grads < 1 || n_grads > FSDP_MAX_RANKS)
+    return fail(FSDP_ERR_INVALID_ARG, "n_grads must be in [1, %d] (got %d)", FSDP_MAX_RANKS,
+                n_grads);
+  if (!grads) return fail(FSDP_ERR_INVALID_ARG, "grads array is NULL");
+  for (int32_t k = 0; k < n_grads; ++k) {
+    if (!grads[k]) return fail(FSDP_ERR_INVALID_ARG, "grads[%d] is NULL", k);
+    if (reinterpret_cast<uintptr_t>(grads[k]) & 1u)
+      return fail(FSDP_ERR_INVALID_ARG, "grads[%d] is not 2-byte aligned", k);
+    const uint16_t* w = static_cast<const uint16_t*>(grads[k]) + u->begin;
+    a->g[k] = w;
+    ranges->push_back(fsdp::range_of(w, u->valid, 2, false, "grads[" + std::to_string(k) + "]"));
+  }
+  a->n_grads = n_grads;
+  return FSDP_OK;
+}
+
+fsdp_status check_f32(const void* p, const char* name) {
+  if (!p) return fail(FSDP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) & 3u)
+    return fail(FSDP_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+  return FSDP_OK;
+}
+
+bool step_vec_ok(const StepArgs& a, Op op) {
+  bool ok = true;
+  if (op != Op::AdamW)
+    for (int k = 0; k < a.n_grads; ++k) ok = ok && aligned16(a.g[k]);
+  if (op == Op::AdamW) ok = ok && aligned16(a.grad);
+  if (op == Op::Reduce) ok = ok && aligned16(a.out);
+  if (op != Op::Reduce) {
+    ok = ok && aligned16(a.p) && aligned16(a.m) && aligned16(a.v);
+    if (a.w) ok = ok && aligned16(a.w);
+  }
+  return ok;
+}
+
+fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float* exp_avg_sq,
+                        void* w, std::vector<fsdp::ByteRange>* ranges, StepArgs* a) {
+  if (fsdp_status st = check_f32(master, "master")) return st;
+  if (fsdp_status st = check_f32(exp_avg, "exp_avg")) return st;
+  if (fsdp_status st = check_f32(exp_avg_sq, "exp_avg_sq")) return st;
+  if (w && (reinterpret_cast<uintptr_t>(w) & 1u))
+    return fail(FSDP_ERR_INVALID_ARG, "param_bf16_out is not 2-byte aligned");
+  a->p = master;
+  a->m = exp_avg;
+  a->v = exp_avg_sq;
+  a->w = static_cast<uint16_t*>(w);
+  ranges->push_back(fsdp::range_of(master, u->valid, 4, true, "master"));
+  ranges->push_back(fsdp::range_of(exp_avg, u->valid, 4, true, "exp_avg"));
+  ranges->push_back(fsdp::range_of(exp_avg_sq, u->valid, 4, true, "exp_avg_sq"));
+  if (w) ranges->push_back(fsdp::range_of(w, u->valid, 2, true, "param_bf16_out"));
+  return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fsdp_status fsdp_reduce_shard(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
+                              double grad_scale, float* out, hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_f32(out, "out")) return st;
+  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.out = out;
+  a.n = u->valid;
+  a.s.gs = static_cast<float>(grad_scale);
+  return launch_step<Op::Reduce>(a, step_vec_ok(a, Op::Reduce), stream, "fsdp_reduce_shard");
+}
+
+fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* master,
+                             float* exp_avg, float* exp_avg_sq, void* param_bf16_out,
+                             const fsdp_adamw_hparams* hp, hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, false, &hs)) return st;
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_f32(grad, "grad")) return st;
+  ranges.push_back(fsdp::range_of(grad, u->valid, 4, false, "grad"));
+  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
+    return st;
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.grad = grad;
+  a.n = u->valid;
+  a.s = to_device(hs);
+  return launch_step<Op::AdamW>(a, step_vec_ok(a, Op::AdamW), stream, "fsdp_adamw_shard");
+}
+
+fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
+                                    const void* const* grads, float* master, float* exp_avg,
+                                    float* exp_avg_sq, void* param_bf16_out,
+                                    const fsdp_adamw_hparams* hp, hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
+    return st;
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.n = u->valid;
+  a.s = to_device(hs);
+  return launch_step<Op::Fused>(a, step_vec_ok(a, Op::Fused), stream,
+                                "fsdp_reduce_adamw_shard");
+}
+
+fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* const* tensors,
+                             int64_t begin, int64_t len, void* dst, hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (dtype != FSDP_F32 && dtype != FSDP_BF16)
+    return fail(FSDP_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(dtype));
+  const int64_t es = dtype == FSDP_F32 ? 4 : 2;
+  if (begin < 0 || len < 0 || begin > u->padded || len > u->padded - begin)
+    return fail(FSDP_ERR_RANGE, "window [%lld, %lld) outside [0, %lld)",
+                static_cast<long long>(begin), static_cast<long long>(begin + len),
+                static_cast<long long>(u->padded));
+  if (len == 0) return FSDP_OK;
+  if (!tensors) return fail(FSDP_ERR_INVALID_ARG, "tensors array is NULL");
+  if (!dst) return fail(FSDP_ERR_INVALID_ARG, "dst is NULL");
+  if (reinterpret_cast<uintptr_t>(dst) % es)
+    return fail(FSDP_ERR_INVALID_ARG, "dst is not element aligned");
+  std::vector<Piece> pieces;
+  std::vector<fsdp::ByteRange> ranges;
+  ranges.push_back(fsdp::range_of(dst, len, es, true, "dst"));
+  const int64_t end = begin + len;
+  for (int32_t i = 0; i < u->T; ++i) {
+    const int64_t a = std::max(begin, u->offset[i]);
+    const int64_t b = std::min(end, u->offset[i + 1]);
+    if (a >= b) continue;
+    if (!tensors[i]) return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is NULL", i);
+    if (reinterpret_cast<uintptr_t>(tensors[i]) % es)
+      return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is not element aligned", i);
+    const char* src = static_cast<const char*>(tensors[i]) + (a - u->offset[i]) * es;
+    char* d = static_cast<char*>(dst) + (a - begin) * es;
+    pieces.push_back(Piece{src, d, b - a});
+    ranges.push_back(fsdp::range_of(src, b - a, es, false, "tensors[" + std::to_string(i) + "]"));
+  }
+  const int64_t pa = std::max(begin, u->U);
+  if (pa < end) pieces.push_back(Piece{nullptr, static_cast<char*>(dst) + (pa - begin) * es,
+                                       end - pa});
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  return launch_pieces(pieces, dtype == FSDP_F32 ? 0 : 1, stream, "fsdp_flatten_pad");
+}
+
+fsdp_status fsdp_cast_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype,
+                                const void* const* shards, void* const* tensors_bf16,
+                                hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (src_dtype != FSDP_F32 && src_dtype != FSDP_BF16)
+    return fail(FSDP_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(src_dtype));
+  if (!shards) return fail(FSDP_ERR_INVALID_ARG, "shards array is NULL");
+  if (!tensors_bf16) return fail(FSDP_ERR_INVALID_ARG, "tensors array is NULL");
+  const int64_t ss = src_dtype == FSDP_F32 ? 4 : 2;
+  std::vector<Piece> pieces;
+  std::vector<fsdp::ByteRange> ranges;
+  for (int32_t k = 0; k < u->F; ++k) {
+    if (!shards[k]) return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is NULL", k);
+    if (reinterpret_cast<uintptr_t>(shards[k]) % ss)
+      return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is not element aligned", k);
+    const int64_t kv = std::max<int64_t>(0, std::min<int64_t>(u->S, u->U - k * u->S));
+    ranges.push_back(fsdp::range_of(shards[k], kv, ss, false, "shards[" + std::to_string(k) + "]"));
+  }
+  for (int32_t i = 0; i < u->T; ++i) {
+    if (u->numel[i] == 0) continue;
+    if (!tensors_bf16[i]) return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is NULL", i);
+    if (reinterpret_cast<uintptr_t>(tensors_bf16[i]) & 1u)
+      return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is not 2-byte aligned", i);
+    ranges.push_back(fsdp::range_of(tensors_bf16[i], u->numel[i], 2, true,
+                                    "tensors[" + std::to_string(i) + "]"));
+    const int64_t lo = u->offset[i], hi = u->offset[i + 1];
+    for (int64_t k = lo / u->S; k * u->S < hi; ++k) {
+      const int64_t a = std::max(lo, k * u->S);
+      const int64_t b = std::min(hi, (k + 1) * u->S);
+      pieces.push_back(Piece{static_cast<const char*>(shards[k]) + (a - k * u->S) * ss,
+                             static_cast<char*>(tensors_bf16[i]) + (a - lo) * 2, b - a});
+    }
+  }
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  return launch_pieces(pieces, src_dtype == FSDP_F32 ? 2 : 1, stream, "fsdp_cast_unflatten");
+}
+
+}  // extern "C"

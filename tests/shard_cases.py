@@ -1,0 +1,184 @@
+"""Test cases for the GPU parity tests: device inputs and oracle expectations.
+
+Inputs come from ``datagen`` (the host generator for the oracle, its device
+twin to fill HBM). Expected values come only from ``oracle`` evaluated on
+host-generated inputs, either on whole (small) units or on sampled indices of
+full-size units: every step of the path is elementwise in the shard index, so
+a sampled index's whole multi-step trajectory can be recomputed on its own.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import datagen
+from datagen import workloads as W
+from oracle import fsdp_oracle as O
+
+FP32_SENTINEL = 0x7FC00001      # a NaN bit pattern no kernel produces
+BF16_SENTINEL = 0x7FC1
+
+HP = O.AdamW(**W.ADAMW)
+
+
+class Case:
+    """One rank's shard of one unit: shapes, F, rank, contributions, seeds."""
+
+    def __init__(self, shapes, F, rank, n_grads=None, config=0, outliers=False,
+                 grad_sigma=W.GRAD_SIGMA, master_sigma=W.MASTER_SIGMA):
+        self.shapes = [tuple(s) for s in shapes]
+        self.F, self.rank = F, rank
+        self.n_grads = F if n_grads is None else n_grads
+        self.L = O.unit_layout(self.shapes, F, rank)
+        self.config = config
+        self.outliers = outliers
+        self.grad_sigma, self.master_sigma = grad_sigma, master_sigma
+        self.master_seed = datagen.seed_for(config, datagen.KIND_MASTER)
+
+    def grad_seed(self, step):
+        return datagen.seed_for(self.config, datagen.KIND_GRAD, step)
+
+    def outlier_seed(self, step):
+        return datagen.seed_for(self.config, datagen.KIND_OUTLIER, step) if self.outliers else None
+
+    # ---------------- host inputs -------------------------------------------
+    def host_master_tensors(self):
+        return [datagen.normal_f32_host(self.master_seed, i, np.arange(n), self.master_sigma)
+                for i, n in enumerate(self.L.numels)]
+
+    def host_grads(self, step):
+        idx = np.arange(self.L.U)
+        return [datagen.bf16_bits_host(self.grad_seed(step), k, idx, self.grad_sigma,
+                                       self.outlier_seed(step)) for k in range(self.n_grads)]
+
+    def host_master_at(self, g):
+        """Generated master values at flat indices g (tensor lookup by offsets)."""
+        offs = np.asarray(self.L.offsets, dtype=np.int64)
+        tid = np.searchsorted(offs, g, side="right") - 1
+        out = np.empty(g.size, np.float32)
+        for i in np.unique(tid):
+            sel = tid == i
+            out[sel] = datagen.normal_f32_host(self.master_seed, int(i), g[sel] - offs[i],
+                                               self.master_sigma)
+        return out
+
+    def host_grads_at(self, step, g):
+        return [datagen.bf16_bits_host(self.grad_seed(step), k, g, self.grad_sigma,
+                                       self.outlier_seed(step)) for k in range(self.n_grads)]
+
+    # ---------------- device inputs -----------------------------------------
+    def device_master_tensors(self, device="cuda"):
+        ts = []
+        for i, n in enumerate(self.L.numels):
+            t = torch.empty(n, dtype=torch.float32, device=device)
+            datagen.fill_normal_f32_(t, self.master_seed, i, self.master_sigma)
+            ts.append(t)
+        return ts
+
+    def device_grads(self, step, device="cuda", out=None):
+        out = out or [torch.empty(self.L.U, dtype=torch.bfloat16, device=device)
+                      for _ in range(self.n_grads)]
+        for k in range(self.n_grads):
+            datagen.fill_bf16_(out[k], self.grad_seed(step), k, self.grad_sigma,
+                               outlier_seed=self.outlier_seed(step))
+        return out
+
+    # ---------------- oracle expectations -----------------------------------
+    def oracle_full(self, steps, emit=True):
+        """Whole-shard oracle trajectory: list of (p, m, v, w) after each step."""
+        L = self.L
+        lo, hi = L.shard_begin, L.shard_begin + L.shard_valid
+        flat = O.flatten_pad([t.view(np.uint32) for t in self.host_master_tensors()], self.F)
+        p = flat.view(np.float32)[lo:hi].copy()
+        m = np.zeros_like(p)
+        v = np.zeros_like(p)
+        out = []
+        for t in range(1, steps + 1):
+            res = O.reduce_adamw_shard(self.host_grads(t), L, p, m, v, HP, t,
+                                       grad_scale=1.0 / self.n_grads, emit_bf16=emit)
+            p, m, v = res[:3]
+            out.append(res)
+        return out
+
+    def oracle_sampled(self, loc, steps, emit=True):
+        """Oracle trajectory at local shard indices ``loc`` only."""
+        g = self.L.shard_begin + np.asarray(loc, dtype=np.int64)
+        one = O.unit_layout([(g.size,)], 1, 0)
+        p = self.host_master_at(g)
+        m = np.zeros_like(p)
+        v = np.zeros_like(p)
+        out = []
+        for t in range(1, steps + 1):
+            res = O.reduce_adamw_shard(self.host_grads_at(t, g), one, p, m, v, HP, t,
+                                       grad_scale=1.0 / self.n_grads, emit_bf16=emit)
+            p, m, v = res[:3]
+            out.append(res)
+        return out
+
+    def sample_indices(self, n=1 << 16, seed=0):
+        """Random local indices plus both ends and every tensor boundary in the window."""
+        valid = self.L.shard_valid
+        if valid <= n:
+            return np.arange(valid, dtype=np.int64)
+        rng = np.random.default_rng(seed)
+        pts = [rng.integers(0, valid, n), np.arange(16), valid - 1 - np.arange(16)]
+        for off in self.L.offsets:
+            rel = off - self.L.shard_begin
+            pts.append(np.arange(rel - 9, rel + 9))
+        s = np.unique(np.concatenate(pts))
+        return s[(s >= 0) & (s < valid)].astype(np.int64)
+
+
+# ---------------- comparison helpers -------------------------------------------
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def gather(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    return to_np(t[torch.from_numpy(idx).to(t.device)])
+
+
+def assert_rel(got, want, tol=1e-6, what=""):
+    """Element-wise relative error <= tol (exact where the expected value is 0)."""
+    got = np.asarray(got, dtype=np.float32)
+    want = np.asarray(want, dtype=np.float32)
+    assert got.shape == want.shape, what
+    same = got.view(np.uint32) == want.view(np.uint32)
+    g64, w64 = got.astype(np.float64), want.astype(np.float64)
+    err = np.abs(g64 - w64)
+    ok = same | (err <= tol * np.abs(w64))
+    if not ok.all():
+        bad = np.flatnonzero(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} elements beyond rel {tol}; first "
+                             f"at {bad.tolist()}: got {got[bad].tolist()} want {want[bad].tolist()}")
+    return float(same.mean())
+
+
+def bf16_ordinal(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def assert_bf16_ulp(got, want, ulps=1, what=""):
+    got = np.asarray(got, dtype=np.uint16)
+    want = np.asarray(want, dtype=np.uint16)
+    d = np.abs(bf16_ordinal(got) - bf16_ordinal(want))
+    if not (d <= ulps).all():
+        bad = np.flatnonzero(d > ulps)[:5]
+        raise AssertionError(f"{what}: {int((d > ulps).sum())} bf16 values beyond {ulps} ulp; "
+                             f"first at {bad.tolist()}")
+    return float((got == want).mean())
+
+
+def assert_bits(got, want, what=""):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, what
+    neq = got != want
+    if neq.any():
+        bad = np.flatnonzero(neq)[:5]
+        raise AssertionError(f"{what}: {int(neq.sum())} elements differ; first at {bad.tolist()}")

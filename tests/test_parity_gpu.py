@@ -1,0 +1,361 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (fixed by the benchmark spec of the problem):
+* flatten, pad, unflatten, indexing and bf16 copies: bit-exact;
+* fp32 master, exp_avg, exp_avg_sq and the fp32 reduced gradient: relative
+  error <= 1e-6 element-wise (the design target is bit equality; the tests
+  report the bit-equal fraction);
+* emitted bf16 parameters: <= 1 bf16 ulp.
+Small units are compared on every element; full-size units (the 7B block at
+F=8, the F sweep) on sampled indices, in the same launch configuration the
+bench uses.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from datagen import workloads as W
+from oracle import fsdp_oracle as O
+from shard_cases import (BF16_SENTINEL, FP32_SENTINEL, HP, Case, assert_bf16_ulp, assert_bits,
+                         assert_rel, gather, to_np)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sharded_flatparameter_flatten_amd as fsdp  # noqa: E402
+
+HPD = fsdp.AdamWHparams(**W.ADAMW)
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def run_rank(case: Case, steps: int, emit=True, fused=True, grads_buf=None, grads_ready=False):
+    """Init the rank's shard with flatten_pad, then `steps` optimizer steps.
+
+    ``grads_ready``: ``grads_buf`` already holds step 1's rows (one-step runs)."""
+    u = fsdp.Unit(case.shapes, case.F, case.rank)
+    masters = case.device_master_tensors()
+    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.flatten_pad(u, masters, p)
+    del masters
+    m = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    v = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV) if emit else None
+    g32 = None if fused else torch.empty(u.S, dtype=torch.float32, device=DEV)
+    for t in range(1, steps + 1):
+        grads = grads_buf if grads_ready else case.device_grads(t, out=grads_buf)
+        if fused:
+            fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, t)
+        else:
+            fsdp.reduce_shard(u, grads, g32)
+            fsdp.adamw_shard(u, g32, p, m, v, w, HPD, t)
+    torch.cuda.synchronize()
+    return u, p, m, v, w
+
+
+def compare_full(case, got, want, emit=True):
+    u, p, m, v, w = got
+    n = u.shard_valid
+    pw, mw, vw = want[:3]
+    fr = [assert_rel(to_np(p)[:n], pw, what="master"),
+          assert_rel(to_np(m)[:n], mw, what="exp_avg"),
+          assert_rel(to_np(v)[:n], vw, what="exp_avg_sq")]
+    if emit:
+        fr.append(assert_bf16_ulp(to_np(w)[:n], want[3], what="bf16 param"))
+    return fr
+
+
+# ---------------------------------------------------------------------------
+# generator twin
+# ---------------------------------------------------------------------------
+
+def test_device_generator_matches_host():
+    seed, oseed = datagen.seed_for(9, 1), datagen.seed_for(9, 2)
+    n = (1 << 24) + 123
+    b = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    datagen.fill_bf16_(b, seed, 5, 1e-3, start=1000, outlier_seed=oseed)
+    f = torch.empty(n, dtype=torch.float32, device=DEV)
+    datagen.fill_normal_f32_(f, seed, 6, 0.02, start=77)
+    idx = np.unique(np.concatenate([np.arange(4096), np.random.default_rng(0).integers(0, n, 1 << 16),
+                                    n - 1 - np.arange(4096)]))
+    assert_bits(gather(b, idx), datagen.bf16_bits_host(seed, 5, idx + 1000, 1e-3, oseed), "bf16")
+    want = datagen.normal_f32_host(seed, 6, idx + 77, 0.02)
+    assert_bits(gather(f, idx).view(np.uint32), want.view(np.uint32), "fp32")
+
+
+# ---------------------------------------------------------------------------
+# tiny unit (every element)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_tiny_fused_three_steps_every_element(rank):
+    case = Case(W.shapes(W.TINY), 4, rank, config=0)
+    log(f"tiny F=4 rank={rank}")
+    got = run_rank(case, 3)
+    want = case.oracle_full(3)[-1]
+    fr = compare_full(case, got, want)
+    log("bit-equal fractions master/m/v/w:", fr)
+
+
+def test_tiny_unfused_matches_oracle_and_fused_bitwise():
+    case = Case(W.shapes(W.TINY), 4, 1, config=0)
+    fused = run_rank(case, 3)
+    unfused = run_rank(case, 3, fused=False)
+    for a, b, name in zip(fused[1:], unfused[1:], ["master", "exp_avg", "exp_avg_sq", "w"]):
+        assert_bits(to_np(a), to_np(b), f"fused vs unfused {name}")
+    compare_full(case, unfused, case.oracle_full(3)[-1])
+
+
+def test_tiny_reduce_shard_every_element():
+    case = Case(W.shapes(W.TINY), 4, 2, config=0)
+    u = fsdp.Unit(case.shapes, 4, 2)
+    grads = case.device_grads(1)
+    out = torch.full((u.S + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    out.view(torch.int32).fill_(FP32_SENTINEL)
+    fsdp.reduce_shard(u, grads, out)
+    torch.cuda.synchronize()
+    want = O.reduce_shard(case.host_grads(1), case.L)
+    fr = assert_rel(to_np(out)[:u.shard_valid], want, what="reduced grad")
+    assert np.all(to_np(out).view(np.uint32)[u.shard_valid:] == FP32_SENTINEL)
+    log("reduce bit-equal fraction", fr)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_tiny_flatten_pad_windows_bit_exact(dtype):
+    rng = np.random.default_rng(4)
+    shapes = W.shapes(W.TINY)
+    F = 4
+    host = [rng.integers(0, 1 << 32, O.numel(s), dtype=np.uint64).astype(np.uint32) for s in shapes]
+    if dtype == torch.bfloat16:
+        host = [h.astype(np.uint16) for h in host]
+        dev = [torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16) for h in host]
+    else:
+        dev = [torch.from_numpy(h.view(np.float32)).to(DEV) for h in host]
+    u = fsdp.Unit(shapes, F, 0)
+    windows = [(r * u.S, u.S) for r in range(F)] + [(0, u.padded), (3, 1001), (262141, 9),
+                                                    (u.U - 5, 5), (1, 0)]
+    for begin, length in windows:
+        dst = torch.empty(max(length, 1), dtype=dtype, device=DEV)
+        fsdp.flatten_pad(u, dev, dst, begin, length)
+        torch.cuda.synchronize()
+        want = O.flatten_pad(host, F, begin, length)
+        assert_bits(to_np(dst)[:length].view(want.dtype), want, f"window {begin}+{length}")
+
+
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+def test_tiny_cast_unflatten_bit_exact(src):
+    shapes = W.shapes(W.TINY)
+    F = 4
+    u = fsdp.Unit(shapes, F, 0)
+    rng = np.random.default_rng(5)
+    if src == "fp32":
+        host = [(rng.standard_normal(u.S) * 0.02).astype(np.float32) for _ in range(F)]
+        host[1][:6] = np.array([np.inf, -np.inf, np.nan, -0.0, 3.4e38, 1e-40], np.float32)
+        dev = [torch.from_numpy(h).to(DEV) for h in host]
+    else:
+        host = [rng.integers(0, 1 << 16, u.S, dtype=np.uint64).astype(np.uint16) for _ in range(F)]
+        dev = [torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16) for h in host]
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+    fsdp.cast_unflatten(u, dev, outs)
+    torch.cuda.synchronize()
+    want = O.cast_unflatten(host, O.unit_layout(shapes, F, 0), shapes)
+    for o, wnt, s in zip(outs, want, shapes):
+        assert_bits(to_np(o).reshape(s), wnt, f"tensor {s}")
+
+
+def test_round_trip_flatten_then_unflatten_is_identity():
+    shapes = W.shapes(W.TINY) + [(7,), (3, 5)]
+    for F in (1, 3, 4, 7, 64):
+        rng = np.random.default_rng(F)
+        host = [rng.integers(0, 1 << 16, O.numel(s), dtype=np.uint64).astype(np.uint16)
+                for s in shapes]
+        dev = [torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16) for h in host]
+        units = [fsdp.Unit(shapes, F, r) for r in range(F)]
+        shards = []
+        for u in units:
+            d = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+            fsdp.flatten_pad(u, dev, d)
+            shards.append(d)
+        outs = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+        fsdp.cast_unflatten(units[0], shards, outs)
+        torch.cuda.synchronize()
+        for o, h in zip(outs, host):
+            assert_bits(to_np(o).reshape(-1), h, f"F={F}")
+
+
+# ---------------------------------------------------------------------------
+# ragged, padded, misaligned, many contributions (every element)
+# ---------------------------------------------------------------------------
+
+RAGGED = [
+    ([(5,)], 8, None),                       # U < F: ranks 5..7 hold only pad
+    ([(3, 7), (1,), (0,), (11,)], 3, None),  # S = 11, odd rank windows, empty tensor
+    ([(1000, 3), (17,)], 7, None),           # S = 431: vector head peel and scalar path
+    ([(4095,), (2049,)], 5, None),           # several tiles, ragged tail
+    ([(300, 41)], 13, None),
+    ([(2048 * 3 + 5,)], 2, 9),               # run-time n_grads path (9 rows)
+    ([(5000,)], 4, 12),
+    ([(4096, 3)], 64, 64),                   # F = 64, 64 rows
+    ([(777,)], 1, 33),                       # F = 1 (the DDP point), 33 rows
+]
+
+
+@pytest.mark.parametrize("shapes,F,ng", RAGGED)
+def test_ragged_units_every_rank_every_element(shapes, F, ng):
+    for rank in range(F):
+        case = Case(shapes, F, rank, n_grads=ng, config=5)
+        got = run_rank(case, 2)
+        if case.L.shard_valid == 0:
+            continue
+        want = case.oracle_full(2)[-1]
+        compare_full(case, got, want)
+
+
+def test_misaligned_buffers_take_the_scalar_path_and_match():
+    case = Case([(333,), (64, 9)], 3, 1, config=6)
+    u = fsdp.Unit(case.shapes, 3, 1)
+    n = u.shard_valid
+    big = [torch.empty(u.U + 3, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    grads = [b[1:1 + u.U] for b in big]                # 2-byte aligned, not 16
+    case.device_grads(1, out=grads)
+    flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], 3)
+    p0 = flat.view(np.float32)[u.shard_begin:u.shard_begin + n]
+    store = torch.zeros(4 * (u.S + 4), dtype=torch.float32, device=DEV)
+    p = store[1:1 + u.S]
+    m = store[u.S + 5:2 * u.S + 5]
+    v = store[2 * u.S + 9:3 * u.S + 9]
+    p[:n].copy_(torch.from_numpy(p0))
+    wbig = torch.empty(u.S + 2, dtype=torch.bfloat16, device=DEV)
+    w = wbig[1:1 + u.S]
+    fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, 1)
+    torch.cuda.synchronize()
+    want = case.oracle_full(1)[-1]
+    compare_full(case, (u, p, m, v, w), want)
+
+
+def test_pad_slots_and_neighbours_are_never_touched():
+    # last rank of a padded unit: slots [valid, S) of every output keep their sentinel
+    shapes = [(1000, 3), (18,)]               # U = 3018, S = 432, rank 6 holds 426 + 6 pad
+    case = Case(shapes, 7, 6, config=7)
+    u = fsdp.Unit(shapes, 7, 6)
+    assert u.shard_valid < u.S
+    grads = case.device_grads(1)
+    flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], 7)
+    p = torch.from_numpy(flat.view(np.float32)[u.shard_begin:u.shard_begin + u.S].copy()).to(DEV)
+    m = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    v = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    n = u.shard_valid
+    for t in (p, m, v):
+        t.view(torch.int32)[n:].fill_(FP32_SENTINEL)
+    w.view(torch.int16)[:].fill_(BF16_SENTINEL)
+    fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, 1)
+    torch.cuda.synchronize()
+    for t in (p, m, v):
+        assert np.all(to_np(t).view(np.uint32)[n:] == FP32_SENTINEL)
+    assert np.all(to_np(w)[n:] == BF16_SENTINEL)
+    compare_full(case, (u, p, m, v, w), case.oracle_full(1)[-1])
+
+
+# ---------------------------------------------------------------------------
+# full-size 7B block at F = 8 (sampled indices) and the F sweep
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def blk7_grads():
+    U = O.unit_layout(W.shapes(W.BLK7), 1, 0).U
+    bufs = [torch.empty(U, dtype=torch.bfloat16, device=DEV) for _ in range(8)]
+    yield bufs
+    del bufs
+
+
+@pytest.fixture(scope="module")
+def sweep_grads():
+    """64 rows of the sweep's step-1 gradients (outliers on); row k is rank k's."""
+    case = Case(W.shapes(W.BLK7), 64, 0, config=3, outliers=True)
+    bufs = case.device_grads(1)
+    torch.cuda.synchronize()
+    yield bufs
+    del bufs
+
+
+@pytest.mark.parametrize("rank", [0, 3, 7])
+def test_blk7_f8_two_steps_sampled(rank, blk7_grads):
+    case = Case(W.shapes(W.BLK7), 8, rank, config=1)
+    log(f"blk7 F=8 rank={rank}")
+    u, p, m, v, w = run_rank(case, 2, grads_buf=blk7_grads[:8])
+    loc = case.sample_indices()
+    want = case.oracle_sampled(loc, 2)[-1]
+    fr = [assert_rel(gather(p, loc), want[0], what="master"),
+          assert_rel(gather(m, loc), want[1], what="exp_avg"),
+          assert_rel(gather(v, loc), want[2], what="exp_avg_sq"),
+          assert_bf16_ulp(gather(w, loc), want[3], what="bf16 param")]
+    log("bit-equal fractions", fr, "samples", loc.size)
+
+
+def test_blk7_f8_fused_equals_unfused_full_shard(blk7_grads):
+    case = Case(W.shapes(W.BLK7), 8, 5, config=1)
+    a = run_rank(case, 1, grads_buf=blk7_grads[:8])
+    b = run_rank(case, 1, fused=False, grads_buf=blk7_grads[:8])
+    for x, y, name in zip(a[1:], b[1:], ["master", "exp_avg", "exp_avg_sq", "w"]):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), name
+
+
+def test_blk7_cast_unflatten_full_size_sampled():
+    shapes = W.shapes(W.BLK7)
+    F = 8
+    u = fsdp.Unit(shapes, F, 0)
+    seed = datagen.seed_for(1, 3)
+    shards = []
+    for k in range(F):
+        s = torch.empty(u.S, dtype=torch.float32, device=DEV)
+        datagen.fill_normal_f32_(s, seed, k, 0.02)
+        shards.append(s)
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+    fsdp.cast_unflatten(u, shards, outs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    for i, (o, s) in enumerate(zip(outs, shapes)):
+        n = o.numel()
+        j = np.unique(np.concatenate([rng.integers(0, n, 4096), np.arange(min(n, 16)),
+                                      n - 1 - np.arange(min(n, 16))]))
+        g = u.offsets[i] + j
+        k = g // u.S
+        src = np.empty(j.size, np.float32)
+        for kk in np.unique(k):
+            sel = k == kk
+            src[sel] = datagen.normal_f32_host(seed, int(kk), g[sel] - kk * u.S, 0.02)
+        want = O.bf16_round_nearest_even(src)
+        assert_bits(gather(o.reshape(-1), j), want, f"tensor {i}")
+
+
+@pytest.mark.parametrize("F", [1, 2, 4, 8, 16, 64, 7, 11, 13])
+def test_blk7_sharding_factor_sweep_with_outliers_sampled(F, sweep_grads):
+    for rank in sorted({0, F - 1}):
+        case = Case(W.shapes(W.BLK7), F, rank, config=3, outliers=True)
+        log(f"sweep F={F} rank={rank} S={case.L.S} valid={case.L.shard_valid}")
+        u, p, m, v, w = run_rank(case, 1, grads_buf=sweep_grads[:F], grads_ready=True)
+        loc = case.sample_indices(1 << 15, seed=F)
+        want = case.oracle_sampled(loc, 1)[-1]
+        assert_rel(gather(p, loc), want[0], what="master")
+        assert_rel(gather(m, loc), want[1], what="exp_avg")
+        assert_rel(gather(v, loc), want[2], what="exp_avg_sq")
+        assert_bf16_ulp(gather(w, loc), want[3], what="bf16 param")
+        del p, m, v, w
