@@ -1,0 +1,330 @@
+"""Benchmark of one rank's FlatParameter shard step on one MI355X.
+
+Workload: the Llama-7B-shaped block unit (q/k/v/o 4096x4096, gate/up
+11008x4096, down 4096x11008, two 4096 norms; 202,383,360 params) as one
+FlatParameter, sharding factor F=8, rank 0 (shard of 25,297,920 params),
+8 bf16 gradient rows ~N(0, 1e-3), fp32 master ~N(0, 0.02), AdamW lr 1e-4,
+betas 0.9/0.999, eps 1e-8, wd 0.01. Inputs are synthetic (datagen) and
+resident in HBM before the timed region.
+
+One step = the whole per-unit hot path of the rank:
+  1. fsdp_reduce_adamw_shard: fp32 reduce of the 8 bf16 rows into the shard,
+     AdamW on fp32 master/m/v in place, bf16 emission of the new parameter;
+  2. fsdp_cast_unflatten: the all-gather arithmetic, F bf16 shards (this
+     rank's just emitted) -> the 9 per-tensor bf16 parameters.
+(The indexer and the flatten/pad of the master weights run once at init.)
+
+Prints one JSON line. value = shard params/s (shard_valid per step / step
+time); roofline = the fused kernel's algorithmic bytes / its average duration
+from HIP events on its stream; cpu_baseline = the CPU oracle on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_reduce_adamw_blk7_f8_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "sharded_flatparameter_flatten_amd", "csrc", "kernels.hip")
+METRIC = "shard step params/s + HBM GB/s (% of peak), 7B-block unit at F=8"
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per fused launch from the committed counter summary, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernels_hip_sha256_16") != kernel_source_hash():
+        return None           # kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
+    """The CPU oracle (as it stands) on the first `sample` elements of the shard."""
+    import numpy as np
+
+    import datagen
+    from datagen import workloads as W
+    from oracle import fsdp_oracle as O
+
+    L = O.unit_layout(W.shapes(W.BLK7), F, rank)
+    n = min(sample, L.shard_valid)
+    g = L.shard_begin + np.arange(n, dtype=np.int64)
+    grads = [datagen.bf16_bits_host(datagen.seed_for(1, 1, 1), k, g, W.GRAD_SIGMA)
+             for k in range(F)]
+    p = datagen.normal_f32_host(datagen.seed_for(1, 0), 0, g, W.MASTER_SIGMA)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    one = O.unit_layout([(n,)], 1, 0)
+    hp = O.AdamW(**W.ADAMW)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.reduce_adamw_shard(grads, one, p, m, v, hp, 1, grad_scale=1.0 / F, emit_bf16=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= 3 and el >= budget_s:
+            break
+    return {
+        "value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+        "sample": (f"fused reduce+AdamW+bf16 emit of the CPU oracle (numpy, one thread) on the "
+                   f"first {n:,} elements of rank {rank}'s shard of the 7B block at F={F}, "
+                   f"{reps} repetitions, {el:.1f} s"),
+    }
+
+
+CALIB_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB)
+
+
+def copy_reference(fsdp, torch, dev, stream, reps=10):
+    cu = fsdp.Unit([(CALIB_ELEMS,)], 1, 0)
+    src = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        fsdp.flatten_pad(cu, [src], dst, stream=stream)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(reps):
+        fsdp.flatten_pad(cu, [src], dst, stream=stream)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * 4 * CALIB_ELEMS * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {path}")
+    rows = []
+    for f in files:
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, match, counter):
+    """Counter value (summed over its instances) per dispatch of kernels matching `match`."""
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not match(r):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
+    """Prints the traffic summary (markdown + JSON block) from two rocprofv3 --pmc runs."""
+    import datagen.workloads as W
+    from oracle import fsdp_oracle as O
+
+    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true>" % F)
+    is_fused = lambda r: bool(fused.search(r.get("Kernel_Name", "")))
+    # the calibration copy is by far the largest 4-byte copy the bench launches
+    is_copy = lambda r: "k_segcopy<0>" in r.get("Kernel_Name", "")
+    largest = lambda xs: [x for x in xs if x >= 0.5 * max(xs)] if xs else xs
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    f_fused = _per_dispatch(fr, is_fused, "FETCH_SIZE")
+    w_fused = _per_dispatch(wr, is_fused, "WRITE_SIZE")
+    f_copy = largest(_per_dispatch(fr, is_copy, "FETCH_SIZE"))
+    w_copy = largest(_per_dispatch(wr, is_copy, "WRITE_SIZE"))
+    if not (f_fused and w_fused and f_copy and w_copy):
+        raise SystemExit("missing dispatches: fused %d/%d copy %d/%d" % (
+            len(f_fused), len(w_fused), len(f_copy), len(w_copy)))
+    avg = lambda x: sum(x) / len(x)
+    cal_bytes = 4 * CALIB_ELEMS
+    kf = cal_bytes / (avg(f_copy) * 1024)          # known bytes / counted bytes
+    kw = cal_bytes / (avg(w_copy) * 1024)
+    rd = avg(f_fused) * 1024 * kf
+    wt = avg(w_fused) * 1024 * kw
+    L = O.unit_layout(W.shapes(W.BLK7), F, 0)
+    alg_r, alg_w = (2 * F + 12) * L.shard_valid, 14 * L.shard_valid
+    rec = {
+        "kernel": "k_step_vec<Fused, %d, emit> (fused reduce+AdamW+bf16 emit)" % F,
+        "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, L.shard_valid),
+        "kernels_hip_sha256_16": kernel_source_hash(),
+        "fused_dispatches": [len(f_fused), len(w_fused)],
+        "fetch_kib_per_dispatch": avg(f_fused), "write_kib_per_dispatch": avg(w_fused),
+        "calibration": "k_segcopy<0>, 1 GiB fp32 read + 1 GiB written",
+        "calib_fetch_kib": avg(f_copy), "calib_write_kib": avg(w_copy),
+        "fetch_scale": kf, "write_scale": kw,
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wt,
+        "hbm_bytes_per_launch": rd + wt,
+        "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
+        "traffic_over_algorithmic": (rd + wt) / (alg_r + alg_w),
+    }
+    print("```json\n" + json.dumps(rec, indent=1) + "\n```")
+
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        pmc_summary(sys.argv[2], sys.argv[3])
+        return
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--F", type=int, default=8)
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one rank's shard step on one GPU; --gpus {args.gpus} is not "
+              "supported (the cross-GPU exchange steps are not part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import sharded_flatparameter_flatten_amd as fsdp
+    from datagen import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = W.shapes(W.BLK7)
+    F, rank = args.F, args.rank
+    units = [fsdp.Unit(shapes, F, r) for r in range(F)]
+    u = units[rank]
+    S, n = u.S, u.shard_valid
+    print(f"# workload blk7 U={u.U} F={F} rank={rank} S={S} valid={n}", file=sys.stderr,
+          flush=True)
+
+    # ---- inputs resident in HBM ------------------------------------------
+    grads = [torch.empty(u.U, dtype=torch.bfloat16, device=dev) for _ in range(F)]
+    for k in range(F):
+        datagen.fill_bf16_(grads[k], datagen.seed_for(1, 1, 1), k, W.GRAD_SIGMA)
+    masters = []
+    for i, nel in enumerate(u.numels):
+        t = torch.empty(nel, dtype=torch.float32, device=dev)
+        datagen.fill_normal_f32_(t, datagen.seed_for(1, 0), i, W.MASTER_SIGMA)
+        masters.append(t)
+    p = torch.empty(S, dtype=torch.float32, device=dev)
+    fsdp.flatten_pad(u, masters, p)                       # init: flatten + pad (once)
+    masters_bf16 = [t.to(torch.bfloat16) for t in masters]
+    shards = []
+    for r in range(F):                                    # every rank's bf16 parameter shard
+        s = torch.empty(S, dtype=torch.bfloat16, device=dev)
+        fsdp.flatten_pad(units[r], masters_bf16, s)
+        shards.append(s)
+    del masters, masters_bf16
+    m = torch.zeros(S, dtype=torch.float32, device=dev)
+    v = torch.zeros(S, dtype=torch.float32, device=dev)
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+    hp = fsdp.AdamWHparams(**W.ADAMW)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, shards[rank], hp, t, stream=stream)
+        fsdp.cast_unflatten(u, shards, outs, stream=stream)
+
+    for i in range(args.warmup):
+        step(i + 1)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, shards[rank], hp, args.warmup + i + 1,
+                                stream=stream)
+        e1.record(stream)
+        fsdp.cast_unflatten(u, shards, outs, stream=stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fused_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    gather_ms = [b.elapsed_time(c) for _, b, c in ev]
+    fused_avg = sum(fused_ms) / K
+    gather_avg = sum(gather_ms) / K
+    ms_per_step = elapsed * 1e3 / K
+
+    # ---- reference: the library's plain 4-byte copy of 1 GiB (same run) ----
+    # (one tensor, F = 1: fsdp_flatten_pad is then a straight copy; its
+    # counters also calibrate the HBM traffic figures)
+    copy_gbps = copy_reference(fsdp, torch, dev, stream)
+
+    fused_bytes = (2 * F + 26) * n                # bf16 rows + fp32 p/m/v in/out + bf16 out
+    gather_bytes = 4 * u.U                        # bf16 in (F*S valid) + bf16 out
+    achieved = fused_bytes / (fused_avg * 1e-3) / 1e9
+    traffic = read_traffic()
+    result = {
+        "metric": METRIC,
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator; bf16 grads, fp32 master)",
+        "config": {
+            "workload": (f"Llama-7B-shaped block unit (202,383,360 params, 9 tensors) as one "
+                         f"FlatParameter, F={F}, rank {rank}: fused reduce+AdamW+bf16 emit on "
+                         f"the {n:,}-param shard, then cast/unflatten of the {F} bf16 shards"),
+            "F": F, "rank": rank, "n_grads": F, "unit_params": u.U, "shard_params": n,
+            "param_dtype": "bf16", "reduce_dtype": "f32",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "fused reduce+AdamW+bf16 emit (k_step_vec<Fused, 8, emit>)",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": fused_bytes,
+            "avg_launch_us": fused_avg * 1e3,
+        },
+        "fused_us": fused_avg * 1e3,
+        "fused_us_min": min(fused_ms) * 1e3,
+        "gather_us": gather_avg * 1e3,
+        "gather_GBps": gather_bytes / (gather_avg * 1e-3) / 1e9,
+        "step_GBps": (fused_bytes + gather_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "unit_params_per_s": u.U / (ms_per_step * 1e-3),
+        "copy_GBps": copy_gbps,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(F, rank, args.cpu_sample, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -38,15 +38,36 @@
 #ifndef FSDP_GRID_CAP
 #define FSDP_GRID_CAP 0   // 0: one workgroup per tile; otherwise a grid-stride cap
 #endif
+#ifndef FSDP_COPY_BLOCK
+#define FSDP_COPY_BLOCK 256   // threads per workgroup, copy kernels
+#endif
+#ifndef FSDP_STEP_BLOCK
+#define FSDP_STEP_BLOCK 256   // threads per workgroup, reduce/AdamW kernels
+#endif
+#ifndef FSDP_STEP_VEC
+#define FSDP_STEP_VEC 4       // consecutive elements per lane in the step kernels (4 or 8)
+#endif
+#ifndef FSDP_NT_LOAD
+#define FSDP_NT_LOAD 0    // 1: streaming (nontemporal) hint on 128-bit loads
+#endif
+#ifndef FSDP_STEP_NT_STORE
+#define FSDP_STEP_NT_STORE 1   // streaming hint on the step kernels' 128-bit stores
+#endif
+#ifndef FSDP_COPY_NT_STORE
+#define FSDP_COPY_NT_STORE 0   // streaming hint on the copy kernels' 128-bit stores
+#endif
 
 using fsdp::fail;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVec = 8;
-constexpr int64_t kTile = int64_t(kThreads) * kVec;
+constexpr int kThreads = FSDP_COPY_BLOCK;
+constexpr int kStepThreads = FSDP_STEP_BLOCK;
+constexpr int kSV = FSDP_STEP_VEC;
+constexpr int64_t kStepTile = int64_t(kStepThreads) * kSV;
+static_assert(kSV == 4 || kSV == 8, "step kernels move 4 or 8 elements per lane");
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -95,12 +116,19 @@ __device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, con
 
 template <typename V>
 __device__ __forceinline__ V ld(const void* p) {
+#if FSDP_NT_LOAD
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#else
   return *reinterpret_cast<const V*>(p);
+#endif
 }
-template <typename V>
+template <typename V, bool NT>
 __device__ __forceinline__ void st(void* p, V x) {
-  *reinterpret_cast<V*>(p) = x;
+  if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<V*>(p));
+  else *reinterpret_cast<V*>(p) = x;
 }
+constexpr bool kStepNt = FSDP_STEP_NT_STORE != 0;
+constexpr bool kCopyNt = FSDP_COPY_NT_STORE != 0;
 
 __device__ __forceinline__ void unpack8(u32x4 q, float (&x)[8]) {
   x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
@@ -116,20 +144,53 @@ __device__ __forceinline__ void accumulate8(u32x4 q, float (&x)[8]) {
   x[6] = x[6] + lo_bf16(q.w); x[7] = x[7] + hi_bf16(q.w);
 }
 
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  const f32x4 a = ld<f32x4>(p), b = ld<f32x4>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
-__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
-  st<f32x4>(p, f32x4{x[0], x[1], x[2], x[3]});
-  st<f32x4>(p + 4, f32x4{x[4], x[5], x[6], x[7]});
-}
-
+template <bool NT>
 __device__ __forceinline__ void store8_bf16(uint16_t* p, const float (&x)[8]) {
-  st<u32x4>(p, u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
-                     pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])});
+  st<u32x4, NT>(p, u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                         pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])});
+}
+
+// Width-generic forms for the step kernels: a lane's SV consecutive elements
+// are one 8-byte (SV = 4) or 16-byte (SV = 8) bf16 access and SV/4 16-byte
+// fp32 accesses.
+template <int SV>
+struct BfVec;
+template <>
+struct BfVec<4> { using T = u32x2; };
+template <>
+struct BfVec<8> { using T = u32x4; };
+
+[[maybe_unused]] __device__ __forceinline__ void unpack(u32x2 q, float (&x)[4]) {
+  x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
+  x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
+}
+[[maybe_unused]] __device__ __forceinline__ void unpack(u32x4 q, float (&x)[8]) { unpack8(q, x); }
+[[maybe_unused]] __device__ __forceinline__ void accumulate(u32x2 q, float (&x)[4]) {
+  x[0] = x[0] + lo_bf16(q.x); x[1] = x[1] + hi_bf16(q.x);
+  x[2] = x[2] + lo_bf16(q.y); x[3] = x[3] + hi_bf16(q.y);
+}
+[[maybe_unused]] __device__ __forceinline__ void accumulate(u32x4 q, float (&x)[8]) {
+  accumulate8(q, x);
+}
+
+template <int SV>
+__device__ __forceinline__ void loadf(const float* p, float (&x)[SV]) {
+#pragma unroll
+  for (int h = 0; h < SV / 4; ++h) {
+    const f32x4 a = ld<f32x4>(p + 4 * h);
+    x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
+  }
+}
+template <int SV, bool NT>
+__device__ __forceinline__ void storef(float* p, const float (&x)[SV]) {
+#pragma unroll
+  for (int h = 0; h < SV / 4; ++h)
+    st<f32x4, NT>(p + 4 * h, f32x4{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]});
+}
+template <int SV, bool NT>
+__device__ __forceinline__ void store_bf16(uint16_t* p, const float (&x)[SV]) {
+  if constexpr (SV == 4) st<u32x2, NT>(p, u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
+  else store8_bf16<NT>(p, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -152,33 +213,34 @@ struct StepArgs {
 
 enum class Op { Reduce, AdamW, Fused };
 
-// Left fold of the gradient rows for 8 consecutive elements at i. NG > 0 is
+// Left fold of the gradient rows for SV consecutive elements at i. NG > 0 is
 // the compile-time count (all loads issued before the first add); NG == 0
 // reads the count at run time and walks the rows in chunks of 8.
-template <int NG>
-__device__ __forceinline__ void reduce8(const StepArgs& a, int64_t i, float (&acc)[8]) {
+template <int NG, int SV>
+__device__ __forceinline__ void reduce_rows(const StepArgs& a, int64_t i, float (&acc)[SV]) {
+  using G = typename BfVec<SV>::T;
   if constexpr (NG > 0) {
-    u32x4 q[NG];
+    G q[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) q[k] = ld<u32x4>(a.g[k] + i);
-    unpack8(q[0], acc);
+    for (int k = 0; k < NG; ++k) q[k] = ld<G>(a.g[k] + i);
+    unpack(q[0], acc);
 #pragma unroll
-    for (int k = 1; k < NG; ++k) accumulate8(q[k], acc);
+    for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
   } else {
     const int ng = a.n_grads;
-    unpack8(ld<u32x4>(a.g[0] + i), acc);
+    unpack(ld<G>(a.g[0] + i), acc);
     int k = 1;
     for (; k + 8 <= ng; k += 8) {
-      u32x4 q[8];
+      G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ld<u32x4>(a.g[k + j] + i);
+      for (int j = 0; j < 8; ++j) q[j] = ld<G>(a.g[k + j] + i);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) accumulate8(q[j], acc);
+      for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
     }
-    for (; k < ng; ++k) accumulate8(ld<u32x4>(a.g[k] + i), acc);
+    for (; k < ng; ++k) accumulate(ld<G>(a.g[k] + i), acc);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a.s.gs;
+  for (int e = 0; e < SV; ++e) acc[e] = acc[e] * a.s.gs;
 }
 
 template <Op OP>
@@ -203,34 +265,36 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
   }
 }
 
-// Vector path: every buffer 16-byte aligned. Thread t of a tile owns elements
-// [tile + 8t, tile + 8t + 8); the last partial group falls back to scalars.
+// Vector path: bf16 rows aligned to 2*kSV bytes, fp32 buffers to 16 bytes.
+// Lane t of a tile owns elements [tile + kSV*t, tile + kSV*t + kSV), so every
+// load and store instruction of a wavefront covers one contiguous range; the
+// last partial group falls back to scalars.
 template <Op OP, int NG, bool EMIT>
-__global__ __launch_bounds__(kThreads) void k_step_vec(StepArgs a) {
+__global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
-  const int64_t stride = int64_t(gridDim.x) * kTile;
-  for (int64_t i = int64_t(blockIdx.x) * kTile + int64_t(threadIdx.x) * kVec; i < n;
+  const int64_t stride = int64_t(gridDim.x) * kStepTile;
+  for (int64_t i = int64_t(blockIdx.x) * kStepTile + int64_t(threadIdx.x) * kSV; i < n;
        i += stride) {
-    if (i + kVec <= n) {
-      float g[8];
+    if (i + kSV <= n) {
+      float g[kSV];
       if constexpr (OP == Op::AdamW) {
-        load8(a.grad + i, g);
+        loadf<kSV>(a.grad + i, g);
       } else {
-        reduce8<NG>(a, i, g);
+        reduce_rows<NG, kSV>(a, i, g);
       }
       if constexpr (OP == Op::Reduce) {
-        store8(a.out + i, g);
+        storef<kSV, kStepNt>(a.out + i, g);
       } else {
-        float p[8], m[8], v[8];
-        load8(a.p + i, p);
-        load8(a.m + i, m);
-        load8(a.v + i, v);
+        float p[kSV], m[kSV], v[kSV];
+        loadf<kSV>(a.p + i, p);
+        loadf<kSV>(a.m + i, m);
+        loadf<kSV>(a.v + i, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
-        store8(a.p + i, p);
-        store8(a.m + i, m);
-        store8(a.v + i, v);
-        if constexpr (EMIT) store8_bf16(a.w + i, p);
+        for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
+        storef<kSV, kStepNt>(a.p + i, p);
+        storef<kSV, kStepNt>(a.m + i, m);
+        storef<kSV, kStepNt>(a.v + i, v);
+        if constexpr (EMIT) store_bf16<kSV, kStepNt>(a.w + i, p);
       }
     } else {
       for (int64_t j = i; j < n; ++j) step_scalar<OP>(a, j);
@@ -238,16 +302,16 @@ __global__ __launch_bounds__(kThreads) void k_step_vec(StepArgs a) {
   }
 }
 
-// Scalar path for unaligned buffers: element tile + j*256 + t, so each
-// instruction of a wavefront still touches 64 consecutive elements.
+// Scalar path for unaligned buffers: element tile + j*kStepThreads + t, so
+// each instruction of a wavefront still touches 64 consecutive elements.
 template <Op OP>
-__global__ __launch_bounds__(kThreads) void k_step_scalar(StepArgs a) {
+__global__ __launch_bounds__(kStepThreads) void k_step_scalar(StepArgs a) {
   const int64_t n = a.n;
-  const int64_t stride = int64_t(gridDim.x) * kTile;
-  for (int64_t base = int64_t(blockIdx.x) * kTile; base < n; base += stride) {
+  const int64_t stride = int64_t(gridDim.x) * kStepTile;
+  for (int64_t base = int64_t(blockIdx.x) * kStepTile; base < n; base += stride) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int64_t i = base + int64_t(j) * kThreads + threadIdx.x;
+    for (int j = 0; j < kSV; ++j) {
+      const int64_t i = base + int64_t(j) * kStepThreads + threadIdx.x;
       if (i < n) step_scalar<OP>(a, i);
     }
   }
@@ -278,72 +342,77 @@ struct SegArgs {
 };
 
 // KIND 0: 4-byte bit copy; 1: 2-byte bit copy; 2: fp32 -> bf16 (nearest even).
+// A lane moves EPL consecutive elements: exactly one 16-byte source vector,
+// so every load (and store) instruction of a wavefront is one contiguous
+// range and no cache line is written in pieces by different instructions.
 template <int KIND>
 struct CopyKind;
 template <>
 struct CopyKind<0> {
   using S = uint32_t;
   using D = uint32_t;
+  static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return x; }
+  static __device__ __forceinline__ void vec(const S* s, D* d) {
+    st<u32x4, kCopyNt>(d, ld<u32x4>(s));
+  }
+  static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
 };
 template <>
 struct CopyKind<1> {
   using S = uint16_t;
   using D = uint16_t;
+  static constexpr int EPL = 8;
   static __device__ __forceinline__ D cvt(S x) { return x; }
+  static __device__ __forceinline__ void vec(const S* s, D* d) {
+    st<u32x4, kCopyNt>(d, ld<u32x4>(s));
+  }
+  static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
 };
 template <>
 struct CopyKind<2> {
   using S = float;
   using D = uint16_t;
+  static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return static_cast<uint16_t>(to_bf16(x)); }
+  static __device__ __forceinline__ void vec(const S* s, D* d) {
+    const f32x4 x = ld<f32x4>(s);
+    st<u32x2, kCopyNt>(d, u32x2{pack_bf16(x.x, x.y), pack_bf16(x.z, x.w)});
+  }
+  static __device__ __forceinline__ void zero(D* d) { st<u32x2, kCopyNt>(d, u32x2{0u, 0u}); }
 };
 
-template <int KIND>
-__device__ __forceinline__ void copy8(const void* src, void* dst) {
-  if constexpr (KIND == 0) {
-    st<u32x4>(dst, ld<u32x4>(src));
-    st<u32x4>(static_cast<uint32_t*>(dst) + 4, ld<u32x4>(static_cast<const uint32_t*>(src) + 4));
-  } else if constexpr (KIND == 1) {
-    st<u32x4>(dst, ld<u32x4>(src));
-  } else {
-    float x[8];
-    load8(static_cast<const float*>(src), x);
-    store8_bf16(static_cast<uint16_t*>(dst), x);
-  }
-}
-
-template <int KIND>
-__device__ __forceinline__ void zero8(void* dst) {
-  st<u32x4>(dst, u32x4{0u, 0u, 0u, 0u});
-  if constexpr (KIND == 0) st<u32x4>(static_cast<uint32_t*>(dst) + 4, u32x4{0u, 0u, 0u, 0u});
-}
+// Elements per lane, and per workgroup tile, of each copy kind (host and device).
+constexpr int copy_epl(int kind) { return kind == 1 ? 8 : 4; }
+constexpr int64_t copy_tile(int kind) { return int64_t(kThreads) * copy_epl(kind); }
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
   using K = CopyKind<KIND>;
   using S = typename K::S;
   using D = typename K::D;
+  constexpr int EPL = K::EPL;
+  constexpr int64_t TILE = int64_t(kThreads) * EPL;
   int s = 0;
   for (int64_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
     while (t >= a.seg[s].tile_end) ++s;   // workgroup-uniform cursor
     const int64_t tile0 = s == 0 ? 0 : a.seg[s - 1].tile_end;
-    const int64_t base = (t - tile0) * kTile;
+    const int64_t base = (t - tile0) * TILE;
     const int64_t len = a.seg[s].len;
     const int32_t mode = a.seg[s].mode;
     const S* src = static_cast<const S*>(a.seg[s].src);
     D* dst = static_cast<D*>(a.seg[s].dst);
     if (mode == kSegVec || mode == kSegZeroVec) {
-      const int64_t i = base + int64_t(threadIdx.x) * kVec;
-      if (i + kVec <= len) {
-        if (mode == kSegVec) copy8<KIND>(src + i, dst + i);
-        else zero8<KIND>(dst + i);
+      const int64_t i = base + int64_t(threadIdx.x) * EPL;
+      if (i + EPL <= len) {
+        if (mode == kSegVec) K::vec(src + i, dst + i);
+        else K::zero(dst + i);
       } else {
         for (int64_t j = i; j < len; ++j) dst[j] = mode == kSegVec ? K::cvt(src[j]) : D(0);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) {
+      for (int j = 0; j < EPL; ++j) {
         const int64_t e = base + int64_t(j) * kThreads + threadIdx.x;
         if (e < len) dst[e] = mode == kSegScalar ? K::cvt(src[e]) : D(0);
       }
@@ -356,6 +425,10 @@ __global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
 // ---------------------------------------------------------------------------
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// a lane's kSV bf16 elements form one 2*kSV-byte access
+bool aligned_bf16_vec(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & uintptr_t(2 * kSV - 1)) == 0;
+}
 
 unsigned grid_for(int64_t tiles) {
   int64_t g = tiles;
@@ -373,11 +446,11 @@ fsdp_status after_launch(const char* what) {
 template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, kThreads, 0, stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, kThreads, 0, stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -388,7 +461,7 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, kThreads, 0, stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
   }
   }
 }
@@ -396,12 +469,12 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
 template <Op OP>
 fsdp_status launch_step(const StepArgs& a, bool vec, hipStream_t stream, const char* what) {
   if (a.n <= 0) return FSDP_OK;
-  const unsigned grid = grid_for((a.n + kTile - 1) / kTile);
+  const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);
   if (vec) {
     if (a.w) launch_vec_ng<OP, true>(a, grid, stream);
     else launch_vec_ng<OP, false>(a, grid, stream);
   } else {
-    k_step_scalar<OP><<<grid, kThreads, 0, stream>>>(a);
+    k_step_scalar<OP><<<grid, kStepThreads, 0, stream>>>(a);
   }
   return after_launch(what);
 }
@@ -412,13 +485,16 @@ struct Piece {
   int64_t len;
 };
 
-// Splits each piece into an unaligned scalar head and a 16-byte aligned vector
-// body when some head length h < 8 aligns both sides; otherwise the whole
-// piece is scalar. Then launches the segments in batches of kMaxSeg.
+// Splits each piece into an unaligned scalar head and an aligned vector body
+// (source on 16 bytes, destination on one lane's store width) when some head
+// length h < EPL aligns both sides; otherwise the whole piece is scalar. Then
+// launches the segments in batches of kMaxSeg.
 fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_t stream,
                           const char* what) {
   const int64_t ss = kind == 1 ? 2 : 4;      // source element bytes
   const int64_t ds = kind == 0 ? 4 : 2;      // destination element bytes
+  const int64_t epl = copy_epl(kind);
+  const uintptr_t dmask = uintptr_t(epl * ds - 1);
   std::vector<Seg> segs;
   segs.reserve(pieces.size() * 2);
   for (const Piece& pc : pieces) {
@@ -426,9 +502,9 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(pc.src);
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(pc.dst);
     int64_t head = -1;
-    for (int64_t h = 0; h < kVec && h < pc.len; ++h) {
+    for (int64_t h = 0; h < epl && h < pc.len; ++h) {
       const bool s_ok = pc.src == nullptr || ((s0 + h * ss) & 15u) == 0;
-      const bool d_ok = ((d0 + h * ds) & 15u) == 0;
+      const bool d_ok = ((d0 + h * ds) & dmask) == 0;
       if (s_ok && d_ok) { head = h; break; }
     }
     const int32_t vmode = pc.src ? kSegVec : kSegZeroVec;
@@ -448,7 +524,7 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     int64_t tiles = 0;
     for (size_t j = 0; j < nb; ++j) {
       a.seg[j] = segs[b + j];
-      tiles += (a.seg[j].len + kTile - 1) / kTile;
+      tiles += (a.seg[j].len + copy_tile(kind) - 1) / copy_tile(kind);
       a.seg[j].tile_end = tiles;
     }
     a.nseg = static_cast<int32_t>(nb);
@@ -496,12 +572,12 @@ fsdp_status check_f32(const void* p, const char* name) {
 bool step_vec_ok(const StepArgs& a, Op op) {
   bool ok = true;
   if (op != Op::AdamW)
-    for (int k = 0; k < a.n_grads; ++k) ok = ok && aligned16(a.g[k]);
+    for (int k = 0; k < a.n_grads; ++k) ok = ok && aligned_bf16_vec(a.g[k]);
   if (op == Op::AdamW) ok = ok && aligned16(a.grad);
   if (op == Op::Reduce) ok = ok && aligned16(a.out);
   if (op != Op::Reduce) {
     ok = ok && aligned16(a.p) && aligned16(a.m) && aligned16(a.v);
-    if (a.w) ok = ok && aligned16(a.w);
+    if (a.w) ok = ok && aligned_bf16_vec(a.w);
   }
   return ok;
 }
