@@ -111,6 +111,74 @@ def copy_reference(fsdp, torch, dev, stream, reps=10):
     return 2 * 4 * CALIB_ELEMS * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
+def model_sequence(args):
+    """Whole-model rank shard: one step = fused reduce+AdamW+bf16 emit for every unit in order."""
+    import torch
+
+    import datagen
+    import sharded_flatparameter_flatten_amd as fsdp
+    from datagen import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    F, rank = wl["F"], wl["rank"]
+    dev = torch.device("cuda:0")
+    units = [fsdp.Unit(W.shapes(u), F, rank) for u in wl["units"]]
+    starts = [0]
+    for u in units:
+        starts.append(starts[-1] + u.S)
+    total = starts[-1]
+    print(f"# workload {args.workload}: {len(units)} units, shard {total:,} params", file=sys.stderr,
+          flush=True)
+    p = torch.empty(total, dtype=torch.float32, device=dev)
+    datagen.fill_normal_f32_(p, datagen.seed_for(wl["config"], 0), 0, W.MASTER_SIGMA)
+    m = torch.zeros(total, dtype=torch.float32, device=dev)
+    v = torch.zeros(total, dtype=torch.float32, device=dev)
+    w = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    gseed = datagen.seed_for(wl["config"], 1, 1)
+    arenas = {}
+    for u in units:                      # one set of rows per distinct unit size
+        if u.U not in arenas:
+            rows = [torch.empty(u.U, dtype=torch.bfloat16, device=dev) for _ in range(F)]
+            for k in range(F):
+                datagen.fill_bf16_(rows[k], gseed, 100 * len(arenas) + k, W.GRAD_SIGMA)
+            arenas[u.U] = rows
+    hp = fsdp.AdamWHparams(**W.ADAMW)
+    stream = torch.cuda.current_stream(dev)
+    win = [(p[a:a + u.S], m[a:a + u.S], v[a:a + u.S], w[a:a + u.S])
+           for u, a in zip(units, starts)]
+
+    def step(t):
+        for u, (pp, mm, vv, ww) in zip(units, win):
+            fsdp.reduce_adamw_shard(u, arenas[u.U], pp, mm, vv, ww, hp, t, stream=stream)
+
+    for i in range(args.warmup):
+        step(i + 1)
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(args.warmup + i + 1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / K
+    valid = sum(u.shard_valid for u in units)
+    nbytes = sum((2 * F + 26) * u.shard_valid for u in units)
+    res = {
+        "metric": "model shard step params/s + HBM GB/s", "workload": args.workload,
+        "value": valid / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_step, "wall_ms_per_step": elapsed * 1e3 / K,
+        "units": len(units), "shard_params": valid,
+        "persistent_bytes": sum(u.persistent_bytes for u in units),
+        "algorithmic_bytes_per_step": nbytes, "GBps": nbytes / (ms_step * 1e-3) / 1e9,
+        "frac_of_8TBps": nbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "dtype": "f32", "data": "synthetic",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def _counter_rows(path):
     import csv
     import glob
@@ -187,6 +255,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--F", type=int, default=8)
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -207,6 +276,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload != "blk7":
+        model_sequence(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shapes = W.shapes(W.BLK7)

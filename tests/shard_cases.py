@@ -182,3 +182,91 @@ def assert_bits(got, want, what=""):
     if neq.any():
         bad = np.flatnonzero(neq)[:5]
         raise AssertionError(f"{what}: {int(neq.sum())} elements differ; first at {bad.tolist()}")
+
+
+class ModelShard:
+    """One rank's persistent shard of a whole model: every unit's fp32 master,
+    exp_avg, exp_avg_sq, bf16 parameter and bf16 gradient slot, carved from
+    one slab per kind (unit u at the prefix sum of the shard lengths).
+
+    Inputs: unit u's master comes from tensor streams 256*u + i; all block
+    units share one generated set of gradient rows (streams k) and the root
+    unit has its own (streams 100 + k). Both sides regenerate any element.
+    """
+
+    def __init__(self, units, F, rank, config, device="cuda"):
+        self.units = units
+        self.F, self.rank, self.config = F, rank, config
+        self.L = [O.unit_layout(W.shapes(u), F, rank) for u in units]
+        self.starts = np.concatenate([[0], np.cumsum([L.S for L in self.L])]).astype(np.int64)
+        total = int(self.starts[-1])
+        self.total = total
+        self.master_seed = datagen.seed_for(config, datagen.KIND_MASTER)
+        self.grad_seed = datagen.seed_for(config, datagen.KIND_GRAD, 1)
+        self.p = torch.empty(total, dtype=torch.float32, device=device)
+        self.m = torch.zeros(total, dtype=torch.float32, device=device)
+        self.v = torch.zeros(total, dtype=torch.float32, device=device)
+        self.w = torch.empty(total, dtype=torch.bfloat16, device=device)
+        self.gslot = torch.zeros(total, dtype=torch.bfloat16, device=device)
+        for u, L in enumerate(self.L):
+            self._fill_master(u, L)
+        ublk = max(L.U for L, unit in zip(self.L, units) if unit is not units[-1])
+        self.block_grads = [torch.empty(ublk, dtype=torch.bfloat16, device=device)
+                            for _ in range(F)]
+        for k in range(F):
+            datagen.fill_bf16_(self.block_grads[k], self.grad_seed, k, W.GRAD_SIGMA)
+        self.root_grads = [torch.empty(self.L[-1].U, dtype=torch.bfloat16, device=device)
+                           for _ in range(F)]
+        for k in range(F):
+            datagen.fill_bf16_(self.root_grads[k], self.grad_seed, 100 + k, W.GRAD_SIGMA)
+
+    def _fill_master(self, u, L):
+        lo, hi = L.shard_begin, L.shard_begin + L.shard_valid
+        base = int(self.starts[u])
+        for i in range(len(L.numels)):
+            a, b = max(lo, L.offsets[i]), min(hi, L.offsets[i + 1])
+            if a >= b:
+                continue
+            dst = self.p[base + a - lo: base + b - lo]
+            datagen.fill_normal_f32_(dst, self.master_seed, 256 * u + i, W.MASTER_SIGMA,
+                                     start=a - L.offsets[i])
+
+    def window(self, t, u):
+        b = int(self.starts[u])
+        return t[b:b + self.L[u].S]
+
+    def grads(self, u):
+        return self.root_grads if u == len(self.L) - 1 else self.block_grads
+
+    def persistent_bytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.p, self.m, self.v, self.w,
+                                                          self.gslot))
+
+    def oracle_sampled(self, u, loc):
+        """Oracle's first step of unit u at local shard indices loc."""
+        L = self.L[u]
+        g = L.shard_begin + np.asarray(loc, dtype=np.int64)
+        offs = np.asarray(L.offsets, dtype=np.int64)
+        tid = np.searchsorted(offs, g, side="right") - 1
+        p = np.empty(g.size, np.float32)
+        for i in np.unique(tid):
+            sel = tid == i
+            p[sel] = datagen.normal_f32_host(self.master_seed, 256 * u + int(i), g[sel] - offs[i],
+                                             W.MASTER_SIGMA)
+        base = 100 if u == len(self.L) - 1 else 0
+        rows = [datagen.bf16_bits_host(self.grad_seed, base + k, g, W.GRAD_SIGMA)
+                for k in range(self.F)]
+        z = np.zeros_like(p)
+        one = O.unit_layout([(g.size,)], 1, 0)
+        return O.reduce_adamw_shard(rows, one, p, z, z, HP, 1, grad_scale=1.0 / self.F,
+                                    emit_bf16=True)
+
+    def sample(self, u, n, seed):
+        L = self.L[u]
+        rng = np.random.default_rng(seed)
+        pts = [rng.integers(0, L.shard_valid, n), np.arange(8), L.shard_valid - 1 - np.arange(8)]
+        for off in L.offsets:
+            rel = off - L.shard_begin
+            pts.append(np.arange(rel - 5, rel + 5))
+        s = np.unique(np.concatenate(pts))
+        return s[(s >= 0) & (s < L.shard_valid)].astype(np.int64)

@@ -1,0 +1,68 @@
+"""GPU parity on whole-model rank shards: every unit of the model, in order.
+
+* Llama-7B-shaped rank shard: 32 block units + the root unit (untied
+  embedding, final norm, lm_head), F=8, rank 0, ~842M params;
+* Llama-70B-shaped rank shard: 80 GQA block units + root, F=8, rank 0,
+  ~8.62B params (~138 GB of persistent state resident in HBM).
+One fused reduce + AdamW + bf16 step per unit on one stream; sampled indices
+of every unit (all of them in the named units) are checked against the
+oracle. Persistent bytes allocated equal 16 * sum(S) per the pages' budget.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from datagen import workloads as W
+from shard_cases import ModelShard, assert_bf16_ulp, assert_rel, gather
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sharded_flatparameter_flatten_amd as fsdp  # noqa: E402
+
+HPD = fsdp.AdamWHparams(**W.ADAMW)
+
+
+def run_model(name, full_units, sparse_n):
+    wl = W.WORKLOADS[name]
+    ms = ModelShard(wl["units"], wl["F"], wl["rank"], wl["config"])
+    units = [fsdp.Unit(W.shapes(u), wl["F"], wl["rank"]) for u in wl["units"]]
+    assert [u.S for u in units] == [L.S for L in ms.L]
+    for i, u in enumerate(units):
+        fsdp.reduce_adamw_shard(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
+                                ms.window(ms.v, i), ms.window(ms.w, i), HPD, 1)
+    torch.cuda.synchronize()
+    n_units = len(units)
+    for i in range(n_units):
+        full = i in full_units or i == n_units - 1
+        loc = ms.sample(i, 1 << 15 if full else sparse_n, seed=i)
+        want = ms.oracle_sampled(i, loc)
+        what = f"{name} unit {i}"
+        assert_rel(gather(ms.window(ms.p, i), loc), want[0], what=what + " master")
+        assert_rel(gather(ms.window(ms.m, i), loc), want[1], what=what + " exp_avg")
+        assert_rel(gather(ms.window(ms.v, i), loc), want[2], what=what + " exp_avg_sq")
+        assert_bf16_ulp(gather(ms.window(ms.w, i), loc), want[3], what=what + " bf16")
+    persistent = sum(u.persistent_bytes for u in units)
+    assert ms.persistent_bytes() == persistent
+    print(f"{name}: {n_units} units, {ms.total:,} shard params, persistent {persistent:,} B",
+          flush=True)
+    del ms
+    gc.collect()
+    torch.cuda.empty_cache()
+    return persistent
+
+
+def test_full_7b_rank_shard_every_unit():
+    assert run_model("full7b", {0, 15, 31}, 4096) == 13_476_831_232
+
+
+def test_full_70b_rank_shard_every_unit():
+    free, total = torch.cuda.mem_get_info()
+    if free < 170 * 2**30:
+        pytest.skip(f"needs ~160 GB free HBM, {free / 2**30:.0f} GiB free")
+    assert run_model("full70b", {0, 40, 79}, 2048) == 137_953_296_384
