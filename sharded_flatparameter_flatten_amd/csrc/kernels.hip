@@ -3,19 +3,26 @@
 //
 // Everything on this path streams through HBM once; nothing is a dense
 // contraction, so there is no MFMA here. The design is about bytes:
-//  * each thread owns 8 consecutive elements, so every bf16 gradient load and
-//    every bf16 store is one 128-bit access and every fp32 state array moves in
-//    two 128-bit accesses; a 64-lane wavefront covers 1 KiB of bf16 per load;
-//  * workgroups of 256 threads own contiguous 2048-element tiles, so every
-//    64-byte line is written whole by one wavefront;
+//  * step kernels (reduce, AdamW, fused): each lane owns 4 consecutive shard
+//    elements, so a gradient row is one 8-byte load and each fp32 state array
+//    one 16-byte access; every load and store instruction of a 64-lane
+//    wavefront covers one contiguous range (no line is written in pieces by
+//    different instructions, which costs dearly on the write path);
 //  * the fused step reads the n_grads gradient rows, master, m and v once and
 //    writes master, m, v (and the bf16 parameter) once: the fp32 reduced
 //    gradient never touches memory;
-//  * buffers that are not 16-byte aligned (e.g. a rank window r*S with S odd)
-//    take a lane-strided scalar path, still coalesced per instruction;
+//  * cache policy, chosen by measurement on MI355X: the gradient rows are read
+//    once, so their loads carry the streaming (nontemporal) hint, and so do
+//    all step-kernel stores; the fp32 state loads stay ordinary (the same
+//    lines are written back by the same wave). The copy kernels stream both
+//    ways. This keeps the 256 MB memory-side cache from holding data that is
+//    never reused and cut the 7B-block fused step from ~195 us to ~164 us;
+//  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
+//    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
 //    (source, destination, length) segments (tensor x shard intersections),
-//    passed in kernel arguments and walked per workgroup with a scalar cursor.
+//    passed in kernel arguments and walked per workgroup with a scalar
+//    cursor; each lane moves one 16-byte source vector.
 //
 // Numerics: every floating-point step is one binary32 operation with round to
 // nearest even. The file is compiled with -ffp-contract=off (and the pragma
@@ -35,9 +42,6 @@
 
 #pragma clang fp contract(off)
 
-#ifndef FSDP_GRID_CAP
-#define FSDP_GRID_CAP 0   // 0: one workgroup per tile; otherwise a grid-stride cap
-#endif
 #ifndef FSDP_COPY_BLOCK
 #define FSDP_COPY_BLOCK 256   // threads per workgroup, copy kernels
 #endif
@@ -47,14 +51,20 @@
 #ifndef FSDP_STEP_VEC
 #define FSDP_STEP_VEC 4       // consecutive elements per lane in the step kernels (4 or 8)
 #endif
-#ifndef FSDP_NT_LOAD
-#define FSDP_NT_LOAD 0    // 1: streaming (nontemporal) hint on 128-bit loads
+#ifndef FSDP_GRAD_NT_LOAD
+#define FSDP_GRAD_NT_LOAD 1   // streaming hint on the gradient-row loads (read once)
+#endif
+#ifndef FSDP_STATE_NT_LOAD
+#define FSDP_STATE_NT_LOAD 0  // streaming hint on the fp32 state loads
+#endif
+#ifndef FSDP_COPY_NT_LOAD
+#define FSDP_COPY_NT_LOAD 1   // streaming hint on the copy kernels' source loads
 #endif
 #ifndef FSDP_STEP_NT_STORE
 #define FSDP_STEP_NT_STORE 1   // streaming hint on the step kernels' 128-bit stores
 #endif
 #ifndef FSDP_COPY_NT_STORE
-#define FSDP_COPY_NT_STORE 0   // streaming hint on the copy kernels' 128-bit stores
+#define FSDP_COPY_NT_STORE 1   // streaming hint on the copy kernels' 128-bit stores
 #endif
 
 using fsdp::fail;
@@ -114,13 +124,10 @@ __device__ __forceinline__ void adamw(float g, float& p, float& m, float& v, con
 // memory helpers (128-bit)
 // ---------------------------------------------------------------------------
 
-template <typename V>
-__device__ __forceinline__ V ld(const void* p) {
-#if FSDP_NT_LOAD
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-#else
-  return *reinterpret_cast<const V*>(p);
-#endif
+template <typename V, bool NT>
+__device__ __forceinline__ V ldh(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
 }
 template <typename V, bool NT>
 __device__ __forceinline__ void st(void* p, V x) {
@@ -129,6 +136,9 @@ __device__ __forceinline__ void st(void* p, V x) {
 }
 constexpr bool kStepNt = FSDP_STEP_NT_STORE != 0;
 constexpr bool kCopyNt = FSDP_COPY_NT_STORE != 0;
+constexpr bool kGradNt = FSDP_GRAD_NT_LOAD != 0;
+constexpr bool kCopyNtLoad = FSDP_COPY_NT_LOAD != 0;
+constexpr bool kStateNt = FSDP_STATE_NT_LOAD != 0;
 
 __device__ __forceinline__ void unpack8(u32x4 q, float (&x)[8]) {
   x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
@@ -177,7 +187,7 @@ template <int SV>
 __device__ __forceinline__ void loadf(const float* p, float (&x)[SV]) {
 #pragma unroll
   for (int h = 0; h < SV / 4; ++h) {
-    const f32x4 a = ld<f32x4>(p + 4 * h);
+    const f32x4 a = ldh<f32x4, kStateNt>(p + 4 * h);
     x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
   }
 }
@@ -222,22 +232,22 @@ __device__ __forceinline__ void reduce_rows(const StepArgs& a, int64_t i, float 
   if constexpr (NG > 0) {
     G q[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) q[k] = ld<G>(a.g[k] + i);
+    for (int k = 0; k < NG; ++k) q[k] = ldh<G, kGradNt>(a.g[k] + i);
     unpack(q[0], acc);
 #pragma unroll
     for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
   } else {
     const int ng = a.n_grads;
-    unpack(ld<G>(a.g[0] + i), acc);
+    unpack(ldh<G, kGradNt>(a.g[0] + i), acc);
     int k = 1;
     for (; k + 8 <= ng; k += 8) {
       G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ld<G>(a.g[k + j] + i);
+      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(a.g[k + j] + i);
 #pragma unroll
       for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
     }
-    for (; k < ng; ++k) accumulate(ld<G>(a.g[k] + i), acc);
+    for (; k < ng; ++k) accumulate(ldh<G, kGradNt>(a.g[k] + i), acc);
   }
 #pragma unroll
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * a.s.gs;
@@ -354,7 +364,7 @@ struct CopyKind<0> {
   static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return x; }
   static __device__ __forceinline__ void vec(const S* s, D* d) {
-    st<u32x4, kCopyNt>(d, ld<u32x4>(s));
+    st<u32x4, kCopyNt>(d, ldh<u32x4, kCopyNtLoad>(s));
   }
   static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
 };
@@ -365,7 +375,7 @@ struct CopyKind<1> {
   static constexpr int EPL = 8;
   static __device__ __forceinline__ D cvt(S x) { return x; }
   static __device__ __forceinline__ void vec(const S* s, D* d) {
-    st<u32x4, kCopyNt>(d, ld<u32x4>(s));
+    st<u32x4, kCopyNt>(d, ldh<u32x4, kCopyNtLoad>(s));
   }
   static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
 };
@@ -376,7 +386,7 @@ struct CopyKind<2> {
   static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return static_cast<uint16_t>(to_bf16(x)); }
   static __device__ __forceinline__ void vec(const S* s, D* d) {
-    const f32x4 x = ld<f32x4>(s);
+    const f32x4 x = ldh<f32x4, kCopyNtLoad>(s);
     st<u32x2, kCopyNt>(d, u32x2{pack_bf16(x.x, x.y), pack_bf16(x.z, x.w)});
   }
   static __device__ __forceinline__ void zero(D* d) { st<u32x2, kCopyNt>(d, u32x2{0u, 0u}); }
@@ -430,11 +440,7 @@ bool aligned_bf16_vec(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & uintptr_t(2 * kSV - 1)) == 0;
 }
 
-unsigned grid_for(int64_t tiles) {
-  int64_t g = tiles;
-  if (FSDP_GRID_CAP > 0 && g > FSDP_GRID_CAP) g = FSDP_GRID_CAP;
-  return static_cast<unsigned>(std::max<int64_t>(g, 1));
-}
+unsigned grid_for(int64_t tiles) { return static_cast<unsigned>(std::max<int64_t>(tiles, 1)); }
 
 fsdp_status after_launch(const char* what) {
   const hipError_t e = hipGetLastError();
