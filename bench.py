@@ -179,6 +179,57 @@ def model_sequence(args):
     print(json.dumps(res), flush=True)
 
 
+def sharding_sweep(args):
+    """Fused reduce+AdamW+emit on rank 0 of the 7B block for each F of the sweep."""
+    import torch
+
+    import datagen
+    import sharded_flatparameter_flatten_amd as fsdp
+    from datagen import workloads as W
+
+    wl = W.WORKLOADS["sweep"]
+    dev = torch.device("cuda:0")
+    shapes = W.shapes(W.BLK7)
+    Fs = wl["Fs"] + wl["padded_Fs"]
+    U = fsdp.Unit(shapes, 1, 0).U
+    rows = [torch.empty(U, dtype=torch.bfloat16, device=dev) for _ in range(max(Fs))]
+    gseed, oseed = datagen.seed_for(wl["config"], 1, 1), datagen.seed_for(wl["config"], 2, 1)
+    for k, r in enumerate(rows):
+        datagen.fill_bf16_(r, gseed, k, W.GRAD_SIGMA, outlier_seed=oseed)
+    hp = fsdp.AdamWHparams(**W.ADAMW)
+    stream = torch.cuda.current_stream(dev)
+    out = []
+    for F in Fs:
+        for rank in sorted({0, F - 1}):
+            u = fsdp.Unit(shapes, F, rank)
+            p = torch.empty(u.S, dtype=torch.float32, device=dev)
+            datagen.fill_normal_f32_(p, datagen.seed_for(wl["config"], 0), 0, W.MASTER_SIGMA)
+            m = torch.zeros_like(p)
+            v = torch.zeros_like(p)
+            w = torch.empty(u.S, dtype=torch.bfloat16, device=dev)
+            for i in range(args.warmup):
+                fsdp.reduce_adamw_shard(u, rows[:F], p, m, v, w, hp, i + 1, stream=stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            ev[0].record(stream)
+            for i in range(args.steps):
+                fsdp.reduce_adamw_shard(u, rows[:F], p, m, v, w, hp, args.warmup + i + 1,
+                                        stream=stream)
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps))
+            avg = sum(us) / len(us)
+            nbytes = (2 * F + 26) * u.shard_valid
+            out.append({"F": F, "rank": rank, "S": u.S, "valid": u.shard_valid,
+                        "vector_path": (2 * u.shard_begin) % 8 == 0,
+                        "fused_us_avg": avg, "fused_us_median": us[len(us) // 2],
+                        "bytes": nbytes, "GBps": nbytes / (avg * 1e-6) / 1e9,
+                        "frac_of_8TBps": nbytes / (avg * 1e-6) / 1e9 / PEAK_HBM_GBPS})
+            print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+            del p, m, v, w
+    print(json.dumps({"metric": "fused shard step per sharding factor", "workload": "sweep",
+                      "rows": out}), flush=True)
+
+
 def _counter_rows(path):
     import csv
     import glob
@@ -255,7 +306,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--F", type=int, default=8)
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b"])
+    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -276,6 +327,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "sweep":
+        sharding_sweep(args)
+        return
     if args.workload != "blk7":
         model_sequence(args)
         return

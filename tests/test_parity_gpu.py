@@ -359,3 +359,34 @@ def test_blk7_sharding_factor_sweep_with_outliers_sampled(F, sweep_grads):
         assert_rel(gather(v, loc), want[2], what="exp_avg_sq")
         assert_bf16_ulp(gather(w, loc), want[3], what="bf16 param")
         del p, m, v, w
+
+
+# ---------------------------------------------------------------------------
+# design target: bit equality (stricter than the stated tolerances)
+# ---------------------------------------------------------------------------
+
+def _bits(x):
+    x = np.asarray(x)
+    return x.view(np.uint32) if x.dtype == np.float32 else x
+
+
+@pytest.mark.parametrize("shapes,F,rank,ng", [
+    (W.shapes(W.TINY), 4, 1, None), ([(1000, 3), (17,)], 7, 3, None), ([(5000,)], 4, 2, 12),
+])
+def test_fused_step_is_bit_equal_to_the_oracle(shapes, F, rank, ng):
+    """Same binary32 op order, no contraction, correctly rounded div/sqrt on both sides."""
+    case = Case(shapes, F, rank, n_grads=ng, config=8)
+    u, p, m, v, w = run_rank(case, 3)
+    n = u.shard_valid
+    want = case.oracle_full(3)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"{name} bits")
+
+
+def test_blk7_f8_sampled_bit_equal(blk7_grads):
+    case = Case(W.shapes(W.BLK7), 8, 2, config=1)
+    u, p, m, v, w = run_rank(case, 2, grads_buf=blk7_grads[:8])
+    loc = case.sample_indices()
+    want = case.oracle_sampled(loc, 2)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(gather(got, loc)), _bits(exp), f"{name} bits")
