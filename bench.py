@@ -220,7 +220,7 @@ def sharding_sweep(args):
             avg = sum(us) / len(us)
             nbytes = (2 * F + 26) * u.shard_valid
             out.append({"F": F, "rank": rank, "S": u.S, "valid": u.shard_valid,
-                        "vector_path": (2 * u.shard_begin) % 8 == 0,
+                        "row_path": "vector" if (2 * u.shard_begin) % 8 == 0 else "shifted",
                         "fused_us_avg": avg, "fused_us_median": us[len(us) // 2],
                         "bytes": nbytes, "GBps": nbytes / (avg * 1e-6) / 1e9,
                         "frac_of_8TBps": nbytes / (avg * 1e-6) / 1e9 / PEAK_HBM_GBPS})

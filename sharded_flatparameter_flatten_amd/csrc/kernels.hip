@@ -253,6 +253,48 @@ __device__ __forceinline__ void reduce_rows(const StepArgs& a, int64_t i, float 
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * a.s.gs;
 }
 
+// A gradient row whose rank window does not start on an 8-byte boundary: the
+// lane reads the two aligned 8-byte words that cover its 4 elements and
+// funnel-shifts them together. Callers keep both words inside the window
+// (group index >= 4 and at least 8 elements left), so nothing outside the
+// bytes the step may read is touched.
+__device__ __forceinline__ u32x2 ld_row_shifted(const uint16_t* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(a & ~uintptr_t(7));
+  const unsigned sh = unsigned(a & 7u) * 8u;
+  const uint64_t lo = ldh<uint64_t, kGradNt>(q);
+  const uint64_t hi = ldh<uint64_t, kGradNt>(q + 1);
+  const uint64_t v = sh ? (lo >> sh) | (hi << (64u - sh)) : lo;
+  return u32x2{uint32_t(v), uint32_t(v >> 32)};
+}
+
+template <int NG>
+__device__ __forceinline__ void reduce_rows_shifted(const StepArgs& a, int64_t i,
+                                                    float (&acc)[4]) {
+  if constexpr (NG > 0) {
+    u32x2 q[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) q[k] = ld_row_shifted(a.g[k] + i);
+    unpack(q[0], acc);
+#pragma unroll
+    for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
+  } else {
+    const int ng = a.n_grads;
+    unpack(ld_row_shifted(a.g[0] + i), acc);
+    int k = 1;
+    for (; k + 8 <= ng; k += 8) {
+      u32x2 q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = ld_row_shifted(a.g[k + j] + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
+    }
+    for (; k < ng; ++k) accumulate(ld_row_shifted(a.g[k] + i), acc);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = acc[e] * a.s.gs;
+}
+
 template <Op OP>
 __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
   float g;
@@ -308,6 +350,42 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
       }
     } else {
       for (int64_t j = i; j < n; ++j) step_scalar<OP>(a, j);
+    }
+  }
+}
+
+// Shifted-row path: fp32 state (and the bf16 output) aligned, gradient rows
+// only 2-byte aligned (a rank window r*S with r*S not a multiple of 4). Same
+// lane layout as the vector path with kSV = 4; the first group and the last
+// 8 elements go through the scalar step.
+template <Op OP, int NG, bool EMIT>
+__global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
+  static_assert(OP != Op::AdamW, "only the gradient rows are shifted");
+  constexpr int V = 4;
+  constexpr int64_t TILE = int64_t(kStepThreads) * V;
+  const int64_t n = a.n;
+  const int64_t stride = int64_t(gridDim.x) * TILE;
+  for (int64_t i = int64_t(blockIdx.x) * TILE + int64_t(threadIdx.x) * V; i < n; i += stride) {
+    if (i >= V && i + 2 * V <= n) {
+      float g[V];
+      reduce_rows_shifted<NG>(a, i, g);
+      if constexpr (OP == Op::Reduce) {
+        storef<V, kStepNt>(a.out + i, g);
+      } else {
+        float p[V], m[V], v[V];
+        loadf<V>(a.p + i, p);
+        loadf<V>(a.m + i, m);
+        loadf<V>(a.v + i, v);
+#pragma unroll
+        for (int e = 0; e < V; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
+        storef<V, kStepNt>(a.p + i, p);
+        storef<V, kStepNt>(a.m + i, m);
+        storef<V, kStepNt>(a.v + i, v);
+        if constexpr (EMIT) store_bf16<V, kStepNt>(a.w + i, p);
+      }
+    } else {
+      const int64_t end = i + V < n ? i + V : n;
+      for (int64_t j = i; j < end; ++j) step_scalar<OP>(a, j);
     }
   }
 }
@@ -472,14 +550,42 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   }
 }
 
+template <Op OP, bool EMIT>
+void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
+  switch (a.n_grads) {
+#define FSDP_NG_CASE(K) \
+  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+    FSDP_NG_CASE(1)
+    FSDP_NG_CASE(2)
+    FSDP_NG_CASE(3)
+    FSDP_NG_CASE(4)
+    FSDP_NG_CASE(5)
+    FSDP_NG_CASE(6)
+    FSDP_NG_CASE(7)
+    FSDP_NG_CASE(8)
+    FSDP_NG_CASE(16)
+#undef FSDP_NG_CASE
+    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+  }
+}
+
+enum class Path { Vector, Shifted, Scalar };
+
 template <Op OP>
-fsdp_status launch_step(const StepArgs& a, bool vec, hipStream_t stream, const char* what) {
+fsdp_status launch_step(const StepArgs& a, Path path, hipStream_t stream, const char* what) {
   if (a.n <= 0) return FSDP_OK;
-  const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);
-  if (vec) {
+  if (path == Path::Vector) {
+    const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);
     if (a.w) launch_vec_ng<OP, true>(a, grid, stream);
     else launch_vec_ng<OP, false>(a, grid, stream);
+  } else if (path == Path::Shifted) {
+    if constexpr (OP != Op::AdamW) {
+      const unsigned grid = grid_for((a.n + 4 * kStepThreads - 1) / (4 * kStepThreads));
+      if (a.w) launch_shift_ng<OP, true>(a, grid, stream);
+      else launch_shift_ng<OP, false>(a, grid, stream);
+    }
   } else {
+    const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);
     k_step_scalar<OP><<<grid, kStepThreads, 0, stream>>>(a);
   }
   return after_launch(what);
@@ -575,17 +681,25 @@ fsdp_status check_f32(const void* p, const char* name) {
   return FSDP_OK;
 }
 
-bool step_vec_ok(const StepArgs& a, Op op) {
-  bool ok = true;
-  if (op != Op::AdamW)
-    for (int k = 0; k < a.n_grads; ++k) ok = ok && aligned_bf16_vec(a.g[k]);
-  if (op == Op::AdamW) ok = ok && aligned16(a.grad);
-  if (op == Op::Reduce) ok = ok && aligned16(a.out);
+// Vector when every buffer is aligned for its vector access; Shifted when only
+// gradient rows fall short (the 4-element shifted loads need 2-byte rows);
+// Scalar otherwise.
+Path step_path(const StepArgs& a, Op op) {
+  bool state_ok = true;
+  if (op == Op::AdamW) state_ok = state_ok && aligned16(a.grad);
+  if (op == Op::Reduce) state_ok = state_ok && aligned16(a.out);
   if (op != Op::Reduce) {
-    ok = ok && aligned16(a.p) && aligned16(a.m) && aligned16(a.v);
-    if (a.w) ok = ok && aligned_bf16_vec(a.w);
+    state_ok = state_ok && aligned16(a.p) && aligned16(a.m) && aligned16(a.v);
+    if (a.w) state_ok = state_ok && aligned_bf16_vec(a.w);
   }
-  return ok;
+  if (!state_ok) return Path::Scalar;
+  if (op == Op::AdamW) return Path::Vector;
+  bool rows_ok = true;
+  for (int k = 0; k < a.n_grads; ++k) rows_ok = rows_ok && aligned_bf16_vec(a.g[k]);
+  if (rows_ok) return Path::Vector;
+  // the shifted path moves 4 elements per lane; its w store needs 8 bytes
+  if (kSV == 4 || !a.w || (reinterpret_cast<uintptr_t>(a.w) & 7u) == 0) return Path::Shifted;
+  return Path::Scalar;
 }
 
 fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float* exp_avg_sq,
@@ -624,7 +738,7 @@ fsdp_status fsdp_reduce_shard(const fsdp_unit* u, int32_t n_grads, const void* c
   a.out = out;
   a.n = u->valid;
   a.s.gs = static_cast<float>(grad_scale);
-  return launch_step<Op::Reduce>(a, step_vec_ok(a, Op::Reduce), stream, "fsdp_reduce_shard");
+  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream, "fsdp_reduce_shard");
 }
 
 fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* master,
@@ -644,7 +758,7 @@ fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* maste
   a.grad = grad;
   a.n = u->valid;
   a.s = to_device(hs);
-  return launch_step<Op::AdamW>(a, step_vec_ok(a, Op::AdamW), stream, "fsdp_adamw_shard");
+  return launch_step<Op::AdamW>(a, step_path(a, Op::AdamW), stream, "fsdp_adamw_shard");
 }
 
 fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
@@ -663,7 +777,7 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
   if (fsdp_status st = fsdp::check_alias(ranges)) return st;
   a.n = u->valid;
   a.s = to_device(hs);
-  return launch_step<Op::Fused>(a, step_vec_ok(a, Op::Fused), stream,
+  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
                                 "fsdp_reduce_adamw_shard");
 }
 

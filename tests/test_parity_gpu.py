@@ -390,3 +390,39 @@ def test_blk7_f8_sampled_bit_equal(blk7_grads):
     want = case.oracle_sampled(loc, 2)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
         assert_bits(_bits(gather(got, loc)), _bits(exp), f"{name} bits")
+
+
+# ---------------------------------------------------------------------------
+# gradient rows whose window is not 8-byte aligned (shifted-row vector path)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("ng", [8, 9])
+@pytest.mark.parametrize("fused", [True, False])
+def test_shifted_rows_with_aligned_state(shift, ng, fused):
+    shapes = [(3000, 7), (129,)]
+    F, rank = 4, 1
+    case = Case(shapes, F, rank, n_grads=ng, config=10)
+    u = fsdp.Unit(shapes, F, rank)
+    big = [torch.empty(u.U + 8, dtype=torch.bfloat16, device=DEV) for _ in range(ng)]
+    grads = [b[shift:shift + u.U] for b in big]      # 2*shift bytes past a 512-byte boundary
+    case.device_grads(1, out=grads)
+    flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], F)
+    n = u.shard_valid
+    p = torch.from_numpy(flat.view(np.float32)[u.shard_begin:u.shard_begin + u.S].copy()).to(DEV)
+    m = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    v = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    if fused:
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, 1)
+    else:
+        g32 = torch.full((u.S,), float("nan"), dtype=torch.float32, device=DEV)
+        fsdp.reduce_shard(u, grads, g32)
+        torch.cuda.synchronize()
+        want_g = O.reduce_shard(case.host_grads(1), case.L)
+        assert_bits(to_np(g32)[:n].view(np.uint32), want_g.view(np.uint32), "reduced grad")
+        fsdp.adamw_shard(u, g32, p, m, v, w, HPD, 1)
+    torch.cuda.synchronize()
+    want = case.oracle_full(1)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"{name} bits")
