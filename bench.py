@@ -93,6 +93,30 @@ def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
     }
 
 
+def rotating_rows(torch, datagen, W, unit, n_rows, n_sets, dev, seed, outlier_seed=None):
+    """n_sets sets of n_rows gradient rows whose rank windows are all disjoint.
+
+    The kernels read only [shard_begin, shard_begin + shard_valid) of a row, so
+    each row is a U-long view into one arena, placed so that its window lands
+    on its own stretch of the arena: R*n_rows*S elements are filled instead of
+    R*n_rows*U allocated.
+    """
+    S, U, r0 = unit.S, unit.U, unit.shard_begin
+    S8 = (S + 7) // 8 * 8          # window spacing that keeps every row base 16-byte aligned
+    arena = torch.empty(r0 + n_sets * n_rows * S8 + U, dtype=torch.bfloat16, device=dev)
+    out = []
+    for j in range(n_sets):
+        rows = []
+        for k in range(n_rows):
+            w0 = r0 + (j * n_rows + k) * S8           # window start in the arena
+            row = arena[w0 - r0:w0 - r0 + U]
+            datagen.fill_bf16_(row[r0:r0 + unit.shard_valid], seed, 64 * j + k, W.GRAD_SIGMA,
+                               start=r0, outlier_seed=outlier_seed)
+            rows.append(row)
+        out.append(rows)
+    return out
+
+
 CALIB_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB)
 
 
@@ -180,7 +204,8 @@ def model_sequence(args):
 
 
 def sharding_sweep(args):
-    """Fused reduce+AdamW+emit on rank 0 of the 7B block for each F of the sweep."""
+    """Fused reduce+AdamW+emit on ranks 0 and F-1 of the 7B block for each F of the sweep,
+    visiting `--rotate` independent buffer sets in turn."""
     import torch
 
     import datagen
@@ -191,41 +216,49 @@ def sharding_sweep(args):
     dev = torch.device("cuda:0")
     shapes = W.shapes(W.BLK7)
     Fs = wl["Fs"] + wl["padded_Fs"]
-    U = fsdp.Unit(shapes, 1, 0).U
-    rows = [torch.empty(U, dtype=torch.bfloat16, device=dev) for _ in range(max(Fs))]
+    R = args.rotate
     gseed, oseed = datagen.seed_for(wl["config"], 1, 1), datagen.seed_for(wl["config"], 2, 1)
-    for k, r in enumerate(rows):
-        datagen.fill_bf16_(r, gseed, k, W.GRAD_SIGMA, outlier_seed=oseed)
     hp = fsdp.AdamWHparams(**W.ADAMW)
     stream = torch.cuda.current_stream(dev)
     out = []
     for F in Fs:
         for rank in sorted({0, F - 1}):
             u = fsdp.Unit(shapes, F, rank)
-            p = torch.empty(u.S, dtype=torch.float32, device=dev)
-            datagen.fill_normal_f32_(p, datagen.seed_for(wl["config"], 0), 0, W.MASTER_SIGMA)
-            m = torch.zeros_like(p)
-            v = torch.zeros_like(p)
-            w = torch.empty(u.S, dtype=torch.bfloat16, device=dev)
-            for i in range(args.warmup):
-                fsdp.reduce_adamw_shard(u, rows[:F], p, m, v, w, hp, i + 1, stream=stream)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-            ev[0].record(stream)
-            for i in range(args.steps):
-                fsdp.reduce_adamw_shard(u, rows[:F], p, m, v, w, hp, args.warmup + i + 1,
+            rows = rotating_rows(torch, datagen, W, u, F, R, dev, gseed, outlier_seed=oseed)
+            state = []
+            for j in range(R):
+                p = torch.empty(u.S, dtype=torch.float32, device=dev)
+                datagen.fill_normal_f32_(p, datagen.seed_for(wl["config"], 0), j, W.MASTER_SIGMA)
+                state.append((p, torch.zeros_like(p), torch.zeros_like(p),
+                              torch.empty(u.S, dtype=torch.bfloat16, device=dev)))
+
+            def fused(i):
+                p, m, v, w = state[i % R]
+                fsdp.reduce_adamw_shard(u, rows[i % R], p, m, v, w, hp, i // R + 1,
                                         stream=stream)
+
+            W0 = max(args.warmup, R)
+            for i in range(W0):
+                fused(i)
+            K = max(args.steps, 2 * R)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+            ev[0].record(stream)
+            for i in range(K):
+                fused(W0 + i)
                 ev[i + 1].record(stream)
             torch.cuda.synchronize()
-            us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps))
+            us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(K))
             avg = sum(us) / len(us)
             nbytes = (2 * F + 26) * u.shard_valid
             out.append({"F": F, "rank": rank, "S": u.S, "valid": u.shard_valid,
                         "row_path": "vector" if (2 * u.shard_begin) % 8 == 0 else "shifted",
+                        "rotating_sets": R,
                         "fused_us_avg": avg, "fused_us_median": us[len(us) // 2],
                         "bytes": nbytes, "GBps": nbytes / (avg * 1e-6) / 1e9,
                         "frac_of_8TBps": nbytes / (avg * 1e-6) / 1e9 / PEAK_HBM_GBPS})
             print(json.dumps(out[-1]), file=sys.stderr, flush=True)
-            del p, m, v, w
+            del rows, state
+            torch.cuda.empty_cache()
     print(json.dumps({"metric": "fused shard step per sharding factor", "workload": "sweep",
                       "rows": out}), flush=True)
 
@@ -306,6 +339,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--F", type=int, default=8)
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="independent buffer sets visited in turn (1 = repeat one set)")
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
@@ -336,45 +371,54 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shapes = W.shapes(W.BLK7)
-    F, rank = args.F, args.rank
+    F, rank, R = args.F, args.rank, args.rotate
     units = [fsdp.Unit(shapes, F, r) for r in range(F)]
     u = units[rank]
     S, n = u.S, u.shard_valid
-    print(f"# workload blk7 U={u.U} F={F} rank={rank} S={S} valid={n}", file=sys.stderr,
+    print(f"# workload blk7 U={u.U} F={F} rank={rank} S={S} valid={n} sets={R}", file=sys.stderr,
           flush=True)
 
-    # ---- inputs resident in HBM ------------------------------------------
-    grads = [torch.empty(u.U, dtype=torch.bfloat16, device=dev) for _ in range(F)]
-    for k in range(F):
-        datagen.fill_bf16_(grads[k], datagen.seed_for(1, 1, 1), k, W.GRAD_SIGMA)
-    masters = []
-    for i, nel in enumerate(u.numels):
-        t = torch.empty(nel, dtype=torch.float32, device=dev)
-        datagen.fill_normal_f32_(t, datagen.seed_for(1, 0), i, W.MASTER_SIGMA)
-        masters.append(t)
-    p = torch.empty(S, dtype=torch.float32, device=dev)
-    fsdp.flatten_pad(u, masters, p)                       # init: flatten + pad (once)
-    masters_bf16 = [t.to(torch.bfloat16) for t in masters]
-    shards = []
-    for r in range(F):                                    # every rank's bf16 parameter shard
-        s = torch.empty(S, dtype=torch.bfloat16, device=dev)
-        fsdp.flatten_pad(units[r], masters_bf16, s)
-        shards.append(s)
-    del masters, masters_bf16
-    m = torch.zeros(S, dtype=torch.float32, device=dev)
-    v = torch.zeros(S, dtype=torch.float32, device=dev)
-    outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+    # ---- inputs resident in HBM: R independent sets, visited in turn -------
+    # (every set has its own gradient windows, optimizer state, bf16 shards and
+    # outputs, so no step finds the previous step's data in a cache)
+    row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1))
+    sets = []
+    for j in range(R):
+        masters = []
+        for i, nel in enumerate(u.numels):
+            t = torch.empty(nel, dtype=torch.float32, device=dev)
+            datagen.fill_normal_f32_(t, datagen.seed_for(1, 0), 256 * j + i, W.MASTER_SIGMA)
+            masters.append(t)
+        p = torch.empty(S, dtype=torch.float32, device=dev)
+        fsdp.flatten_pad(u, masters, p)                   # init: flatten + pad (once)
+        masters_bf16 = [t.to(torch.bfloat16) for t in masters]
+        shards = []
+        for r in range(F):                                # every rank's bf16 parameter shard
+            sh = torch.empty(S, dtype=torch.bfloat16, device=dev)
+            fsdp.flatten_pad(units[r], masters_bf16, sh)
+            shards.append(sh)
+        del masters, masters_bf16
+        m = torch.zeros(S, dtype=torch.float32, device=dev)
+        v = torch.zeros(S, dtype=torch.float32, device=dev)
+        outs = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes]
+        sets.append((row_sets[j], p, m, v, shards, outs))
     hp = fsdp.AdamWHparams(**W.ADAMW)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(t):
-        fsdp.reduce_adamw_shard(u, grads, p, m, v, shards[rank], hp, t, stream=stream)
+    def fused(i):
+        grads, p, m, v, shards, outs = sets[i % R]
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, shards[rank], hp, i // R + 1, stream=stream)
+
+    def gather(i):
+        grads, p, m, v, shards, outs = sets[i % R]
         fsdp.cast_unflatten(u, shards, outs, stream=stream)
 
-    for i in range(args.warmup):
-        step(i + 1)
+    W0 = max(args.warmup, R)
+    for i in range(W0):
+        fused(i)
+        gather(i)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -385,10 +429,9 @@ def main():
     for i in range(K):
         e0, e1, e2 = ev[i]
         e0.record(stream)
-        fsdp.reduce_adamw_shard(u, grads, p, m, v, shards[rank], hp, args.warmup + i + 1,
-                                stream=stream)
+        fused(W0 + i)
         e1.record(stream)
-        fsdp.cast_unflatten(u, shards, outs, stream=stream)
+        gather(W0 + i)
         e2.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -425,7 +468,7 @@ def main():
                          f"FlatParameter, F={F}, rank {rank}: fused reduce+AdamW+bf16 emit on "
                          f"the {n:,}-param shard, then cast/unflatten of the {F} bf16 shards"),
             "F": F, "rank": rank, "n_grads": F, "unit_params": u.U, "shard_params": n,
-            "param_dtype": "bf16", "reduce_dtype": "f32",
+            "param_dtype": "bf16", "reduce_dtype": "f32", "rotating_sets": R,
         },
         "roofline": {
             "bound": "hbm",

@@ -11,12 +11,12 @@
 //  * the fused step reads the n_grads gradient rows, master, m and v once and
 //    writes master, m, v (and the bf16 parameter) once: the fp32 reduced
 //    gradient never touches memory;
-//  * cache policy, chosen by measurement on MI355X: the gradient rows are read
-//    once, so their loads carry the streaming (nontemporal) hint, and so do
-//    all step-kernel stores; the fp32 state loads stay ordinary (the same
-//    lines are written back by the same wave). The copy kernels stream both
-//    ways. This keeps the 256 MB memory-side cache from holding data that is
-//    never reused and cut the 7B-block fused step from ~195 us to ~164 us;
+//  * cache policy, chosen by measurement on MI355X with rotating buffer sets
+//    (no reuse between steps): the gradient rows are read once, so their
+//    loads carry the streaming (nontemporal) hint, and so do all step-kernel
+//    stores; the fp32 state loads stay ordinary (the same lines are written
+//    back by the same wave); the copy kernels use ordinary loads and stores.
+//    This cut the 7B-block step (fused + gather) from ~331 us to ~318 us;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
@@ -58,13 +58,13 @@
 #define FSDP_STATE_NT_LOAD 0  // streaming hint on the fp32 state loads
 #endif
 #ifndef FSDP_COPY_NT_LOAD
-#define FSDP_COPY_NT_LOAD 1   // streaming hint on the copy kernels' source loads
+#define FSDP_COPY_NT_LOAD 0    // streaming hint on the copy kernels' source loads
 #endif
 #ifndef FSDP_STEP_NT_STORE
 #define FSDP_STEP_NT_STORE 1   // streaming hint on the step kernels' 128-bit stores
 #endif
 #ifndef FSDP_COPY_NT_STORE
-#define FSDP_COPY_NT_STORE 1   // streaming hint on the copy kernels' 128-bit stores
+#define FSDP_COPY_NT_STORE 0   // streaming hint on the copy kernels' 128-bit stores
 #endif
 
 using fsdp::fail;
