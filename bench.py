@@ -171,9 +171,14 @@ def model_sequence(args):
     win = [(p[a:a + u.S], m[a:a + u.S], v[a:a + u.S], w[a:a + u.S])
            for u, a in zip(units, starts)]
 
+    batch = [(u, arenas[u.U]) + tuple(wn) for u, wn in zip(units, win)]
+
     def step(t):
-        for u, (pp, mm, vv, ww) in zip(units, win):
-            fsdp.reduce_adamw_shard(u, arenas[u.U], pp, mm, vv, ww, hp, t, stream=stream)
+        if args.per_unit:
+            for u, (pp, mm, vv, ww) in zip(units, win):
+                fsdp.reduce_adamw_shard(u, arenas[u.U], pp, mm, vv, ww, hp, t, stream=stream)
+        else:
+            fsdp.reduce_adamw_units(batch, hp, t, stream=stream)
 
     for i in range(args.warmup):
         step(i + 1)
@@ -195,6 +200,8 @@ def model_sequence(args):
         "value": valid / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_step, "wall_ms_per_step": elapsed * 1e3 / K,
         "units": len(units), "shard_params": valid,
+        "entry_point": "fsdp_reduce_adamw_shard per unit" if args.per_unit
+        else "fsdp_reduce_adamw_units (batched launches)",
         "persistent_bytes": sum(u.persistent_bytes for u in units),
         "algorithmic_bytes_per_step": nbytes, "GBps": nbytes / (ms_step * 1e-3) / 1e9,
         "frac_of_8TBps": nbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -342,6 +349,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep"])
+    ap.add_argument("--per-unit", action="store_true",
+                    help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)

@@ -172,6 +172,32 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* unit, int32_t n_grads,
                                     void* param_bf16_out,
                                     const fsdp_adamw_hparams* hp, hipStream_t stream);
 
+/* One unit's share of a multi-unit optimizer step (see fsdp_reduce_adamw_units). */
+typedef struct {
+  const fsdp_unit* unit;
+  const void* const* grads;   /* host array of n_grads device pointers, U elements each */
+  float* master;              /* shard_valid fp32 each, updated in place */
+  float* exp_avg;
+  float* exp_avg_sq;
+  void* param_bf16_out;       /* NULL or shard_valid bf16 outputs */
+} fsdp_unit_step;
+
+/* The rank's optimizer step over many units at once: for every entry, exactly
+ * what fsdp_reduce_adamw_shard computes for it (bitwise), with one set of
+ * hyper-parameters (one step t, one grad_scale) and one n_grads for all.
+ * [FSDP-math, "The backward cycle: all-gather, grads, reduce-scatter"]: after
+ * the last reduce-scatter the optimizer updates every local slice in place;
+ * [FSDP-math, "The sharding unit: FlatParameter and the wrapping policy"]: few
+ * large operations rather than many small ones. Aligned entries with
+ * n_grads <= 8 and fewer than 2^22 shard elements are stepped together, one
+ * kernel launch per up to 30 units; larger or unaligned entries get one
+ * launch each. All entries are validated (including overlaps
+ * between different units' buffers) before anything is enqueued.
+ * n_units == 0 is a no-op. */
+fsdp_status fsdp_reduce_adamw_units(int32_t n_units, const fsdp_unit_step* steps,
+                                    int32_t n_grads, const fsdp_adamw_hparams* hp,
+                                    hipStream_t stream);
+
 /* All-gather arithmetic + unflatten into per-tensor bf16 parameters.
  * [FSDP-math, "The forward cycle: all-gather, compute, reshard"]: each rank
  * contributes its slice and ends with the unit's full weights, used as

@@ -14,6 +14,7 @@ Names follow the C ABI in include/fsdp_shard.h:
                                             -> fsdp_adamw_shard
 * ``reduce_adamw_shard(unit, grads, master, exp_avg, exp_avg_sq, param_out, hp)``
                                             -> fsdp_reduce_adamw_shard
+* ``reduce_adamw_units(steps, hp, step)``   -> fsdp_reduce_adamw_units
 * ``cast_unflatten(unit, shards, outs)``    -> fsdp_cast_unflatten
 """
 
@@ -27,7 +28,7 @@ import torch
 
 __all__ = [
     "FsdpError", "Unit", "AdamWHparams", "flatten_pad", "reduce_shard", "adamw_shard",
-    "reduce_adamw_shard", "cast_unflatten", "abi_version", "library_path",
+    "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "abi_version", "library_path",
     "F32", "BF16",
 ]
 
@@ -52,6 +53,12 @@ class _UnitInfo(ctypes.Structure):
                 ("F", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("n_tensors", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("fingerprint", ctypes.c_uint64)]
+
+
+class _UnitStep(ctypes.Structure):
+    _fields_ = [("unit", ctypes.c_void_p), ("grads", ctypes.POINTER(ctypes.c_void_p)),
+                ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("param_bf16_out", ctypes.c_void_p)]
 
 
 class _Hparams(ctypes.Structure):
@@ -90,6 +97,8 @@ def _load():
         "fsdp_reduce_adamw_shard": (st, [vp, i32, _c_void_p_p, vp, vp, vp, vp,
                                          ctypes.POINTER(_Hparams), vp]),
         "fsdp_cast_unflatten": (st, [vp, st, _c_void_p_p, _c_void_p_p, vp]),
+        "fsdp_reduce_adamw_units": (st, [i32, ctypes.POINTER(_UnitStep), i32,
+                                         ctypes.POINTER(_Hparams), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -151,13 +160,6 @@ class AdamWHparams:
     def _c(self, step: int, grad_scale: float = 0.0) -> _Hparams:
         return _Hparams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
                         grad_scale, int(step))
-
-
-def _shape_numel(shape) -> int:
-    n = 1
-    for d in shape:
-        n *= int(d)
-    return n
 
 
 class Unit:
@@ -255,6 +257,48 @@ def reduce_adamw_shard(unit: Unit, grads, master, exp_avg, exp_avg_sq, param_out
     c = hp._c(step, gs)
     _check(_lib.fsdp_reduce_adamw_shard(unit.handle, len(ptrs), _ptr_array(ptrs), p, m, v, w,
                                         ctypes.byref(c), _stream(stream, master.device)))
+
+
+class UnitsStep:
+    """A multi-unit optimizer step with its arguments marshalled once.
+
+    ``steps``: sequence of (unit, grads, master, exp_avg, exp_avg_sq, param_out or None);
+    every entry uses the same number of gradient rows. The tensors must stay
+    alive (and at the same addresses) while the object is used; each call only
+    fills in the hyper-parameters and the stream."""
+
+    def __init__(self, steps):
+        steps = list(steps)
+        if not steps:
+            raise ValueError("need at least one unit")
+        self.n_grads = len(steps[0][1])
+        self._keep = [steps]
+        self._arr = (_UnitStep * len(steps))()
+        for j, (unit, grads, master, exp_avg, exp_avg_sq, param_out) in enumerate(steps):
+            if len(grads) != self.n_grads:
+                raise ValueError("every unit needs the same number of gradient rows")
+            rows = _ptr_array(_grad_ptrs(unit, grads))
+            self._keep.append(rows)
+            p, m, v, w = _state_ptrs(unit, master, exp_avg, exp_avg_sq, param_out)
+            self._arr[j] = _UnitStep(unit.handle.value,
+                                     ctypes.cast(rows, ctypes.POINTER(ctypes.c_void_p)), p, m, v, w)
+        self.n_units = len(steps)
+        self.device = steps[0][2].device
+
+    def __call__(self, hp: AdamWHparams, step: int, grad_scale: float | None = None,
+                 stream=None):
+        gs = 1.0 / self.n_grads if grad_scale is None else float(grad_scale)
+        c = hp._c(step, gs)
+        _check(_lib.fsdp_reduce_adamw_units(self.n_units, self._arr, self.n_grads,
+                                            ctypes.byref(c), _stream(stream, self.device)))
+
+
+def reduce_adamw_units(steps, hp: AdamWHparams, step: int, grad_scale: float | None = None,
+                       stream=None):
+    """One optimizer step over many units (see UnitsStep for the argument layout)."""
+    steps = list(steps)
+    if steps:
+        UnitsStep(steps)(hp, step, grad_scale, stream)
 
 
 def cast_unflatten(unit: Unit, shards, outs, stream=None):

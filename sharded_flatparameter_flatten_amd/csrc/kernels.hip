@@ -223,34 +223,49 @@ struct StepArgs {
 
 enum class Op { Reduce, AdamW, Fused };
 
-// Left fold of the gradient rows for SV consecutive elements at i. NG > 0 is
-// the compile-time count (all loads issued before the first add); NG == 0
-// reads the count at run time and walks the rows in chunks of 8.
+// Left fold of the gradient rows for SV consecutive elements at i, times gs.
+// NG > 0 is the compile-time count (all loads issued before the first add);
+// NG == 0 reads the count at run time and walks the rows in chunks of 8.
 template <int NG, int SV>
-__device__ __forceinline__ void reduce_rows(const StepArgs& a, int64_t i, float (&acc)[SV]) {
+__device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, float gs,
+                                            int64_t i, float (&acc)[SV]) {
   using G = typename BfVec<SV>::T;
   if constexpr (NG > 0) {
     G q[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) q[k] = ldh<G, kGradNt>(a.g[k] + i);
+    for (int k = 0; k < NG; ++k) q[k] = ldh<G, kGradNt>(g[k] + i);
     unpack(q[0], acc);
 #pragma unroll
     for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
   } else {
-    const int ng = a.n_grads;
-    unpack(ldh<G, kGradNt>(a.g[0] + i), acc);
+    unpack(ldh<G, kGradNt>(g[0] + i), acc);
     int k = 1;
     for (; k + 8 <= ng; k += 8) {
       G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(a.g[k + j] + i);
+      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(g[k + j] + i);
 #pragma unroll
       for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
     }
-    for (; k < ng; ++k) accumulate(ldh<G, kGradNt>(a.g[k] + i), acc);
+    for (; k < ng; ++k) accumulate(ldh<G, kGradNt>(g[k] + i), acc);
   }
 #pragma unroll
-  for (int e = 0; e < SV; ++e) acc[e] = acc[e] * a.s.gs;
+  for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
+}
+
+// One element of the fused step from raw pointers (tails of the vector paths).
+__device__ __forceinline__ void fused_scalar(const uint16_t* const* g, int ng, float* p_,
+                                             float* m_, float* v_, uint16_t* w_, int64_t i,
+                                             const Adam& s) {
+  float gr = widen(g[0][i]);
+  for (int k = 1; k < ng; ++k) gr = gr + widen(g[k][i]);
+  gr = gr * s.gs;
+  float p = p_[i], m = m_[i], v = v_[i];
+  adamw(gr, p, m, v, s);
+  p_[i] = p;
+  m_[i] = m;
+  v_[i] = v;
+  if (w_) w_[i] = static_cast<uint16_t>(to_bf16(p));
 }
 
 // A gradient row whose rank window does not start on an 8-byte boundary: the
@@ -332,7 +347,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
       if constexpr (OP == Op::AdamW) {
         loadf<kSV>(a.grad + i, g);
       } else {
-        reduce_rows<NG, kSV>(a, i, g);
+        reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
       }
       if constexpr (OP == Op::Reduce) {
         storef<kSV, kStepNt>(a.out + i, g);
@@ -401,6 +416,77 @@ __global__ __launch_bounds__(kStepThreads) void k_step_scalar(StepArgs a) {
     for (int j = 0; j < kSV; ++j) {
       const int64_t i = base + int64_t(j) * kStepThreads + threadIdx.x;
       if (i < n) step_scalar<OP>(a, i);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// batched fused step over many units (one launch per up to kMaxMultiUnits)
+// ---------------------------------------------------------------------------
+
+constexpr int kMultiRows = 8;        // row pointers per unit descriptor
+constexpr int kMaxMultiUnits = 30;   // descriptors per launch (kernel arguments < 4 KB)
+// Units at least this long get a launch of their own: there the per-launch
+// cost is negligible and the single-unit kernel, whose pointers sit at fixed
+// kernel-argument offsets, starts its workgroups sooner.
+constexpr int64_t kBatchMaxElems = int64_t(1) << 22;
+
+struct UnitDesc {
+  const uint16_t* g[kMultiRows];     // rank-window start of each contribution
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* w;                       // bf16 parameter out, or null
+  int64_t n;                         // shard_valid
+  int64_t tile_end;                  // exclusive prefix of tiles over the batch
+};
+
+struct MultiArgs {
+  UnitDesc u[kMaxMultiUnits];
+  int64_t tiles;
+  int32_t nu;
+  int32_t n_grads;
+  Adam s;
+};
+
+// Index of the first entry whose exclusive tile prefix exceeds t: a
+// workgroup-uniform binary search over kernel arguments (a handful of
+// dependent scalar loads instead of a linear walk).
+template <typename E>
+__device__ __forceinline__ int find_entry(const E* e, int count, int64_t t) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (t < e[mid].tile_end) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Tiles of all units of the batch laid end to end; a workgroup finds its unit
+// by binary search over the descriptors (scalar registers) and runs the same
+// vector body as k_step_vec<Fused> on it.
+template <int NG>
+__global__ __launch_bounds__(kStepThreads) void k_step_multi(MultiArgs a) {
+  for (int64_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
+    const int s = find_entry(a.u, a.nu, t);
+    const int64_t tile0 = s == 0 ? 0 : a.u[s - 1].tile_end;
+    const UnitDesc& d = a.u[s];
+    const int64_t i = (t - tile0) * kStepTile + int64_t(threadIdx.x) * kSV;
+    if (i + kSV <= d.n) {
+      float g[kSV], p[kSV], m[kSV], v[kSV];
+      reduce_rows<NG, kSV>(d.g, a.n_grads, a.s.gs, i, g);
+      loadf<kSV>(d.p + i, p);
+      loadf<kSV>(d.m + i, m);
+      loadf<kSV>(d.v + i, v);
+#pragma unroll
+      for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
+      storef<kSV, kStepNt>(d.p + i, p);
+      storef<kSV, kStepNt>(d.m + i, m);
+      storef<kSV, kStepNt>(d.v + i, v);
+      if (d.w) store_bf16<kSV, kStepNt>(d.w + i, p);
+    } else {
+      for (int64_t j = i; j < d.n; ++j) fused_scalar(d.g, a.n_grads, d.p, d.m, d.v, d.w, j, a.s);
     }
   }
 }
@@ -481,9 +567,8 @@ __global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
   using D = typename K::D;
   constexpr int EPL = K::EPL;
   constexpr int64_t TILE = int64_t(kThreads) * EPL;
-  int s = 0;
   for (int64_t t = blockIdx.x; t < a.tiles; t += gridDim.x) {
-    while (t >= a.seg[s].tile_end) ++s;   // workgroup-uniform cursor
+    const int s = find_entry(a.seg, a.nseg, t);
     const int64_t tile0 = s == 0 ? 0 : a.seg[s - 1].tile_end;
     const int64_t base = (t - tile0) * TILE;
     const int64_t len = a.seg[s].len;
@@ -652,12 +737,31 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
   return FSDP_OK;
 }
 
+void launch_multi(const MultiArgs& a, hipStream_t stream) {
+  const unsigned grid = grid_for(a.tiles);
+  switch (a.n_grads) {
+#define FSDP_NG_CASE(K) \
+  case K: k_step_multi<K><<<grid, kStepThreads, 0, stream>>>(a); break;
+    FSDP_NG_CASE(1)
+    FSDP_NG_CASE(2)
+    FSDP_NG_CASE(3)
+    FSDP_NG_CASE(4)
+    FSDP_NG_CASE(5)
+    FSDP_NG_CASE(6)
+    FSDP_NG_CASE(7)
+    FSDP_NG_CASE(8)
+#undef FSDP_NG_CASE
+    default: break;   // callers batch only n_grads <= kMultiRows
+  }
+}
+
 Adam to_device(const fsdp::AdamScalars& h) {
   return Adam{h.gs, h.b1, h.omb1, h.b2, h.omb2, h.bc1, h.bc2, h.lr, h.eps, h.wd};
 }
 
 fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
-                        std::vector<fsdp::ByteRange>* ranges, StepArgs* a) {
+                        std::vector<fsdp::ByteRange>* ranges, StepArgs* a,
+                        const std::string& who = "") {
   if (n_grads < 1 || n_grads > FSDP_MAX_RANKS)
     return fail(FSDP_ERR_INVALID_ARG, "n_grads must be in [1, %d] (got %d)", FSDP_MAX_RANKS,
                 n_grads);
@@ -668,7 +772,8 @@ fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* 
       return fail(FSDP_ERR_INVALID_ARG, "grads[%d] is not 2-byte aligned", k);
     const uint16_t* w = static_cast<const uint16_t*>(grads[k]) + u->begin;
     a->g[k] = w;
-    ranges->push_back(fsdp::range_of(w, u->valid, 2, false, "grads[" + std::to_string(k) + "]"));
+    ranges->push_back(
+        fsdp::range_of(w, u->valid, 2, false, who + "grads[" + std::to_string(k) + "]"));
   }
   a->n_grads = n_grads;
   return FSDP_OK;
@@ -703,7 +808,8 @@ Path step_path(const StepArgs& a, Op op) {
 }
 
 fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float* exp_avg_sq,
-                        void* w, std::vector<fsdp::ByteRange>* ranges, StepArgs* a) {
+                        void* w, std::vector<fsdp::ByteRange>* ranges, StepArgs* a,
+                        const std::string& who = "") {
   if (fsdp_status st = check_f32(master, "master")) return st;
   if (fsdp_status st = check_f32(exp_avg, "exp_avg")) return st;
   if (fsdp_status st = check_f32(exp_avg_sq, "exp_avg_sq")) return st;
@@ -713,10 +819,10 @@ fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float
   a->m = exp_avg;
   a->v = exp_avg_sq;
   a->w = static_cast<uint16_t*>(w);
-  ranges->push_back(fsdp::range_of(master, u->valid, 4, true, "master"));
-  ranges->push_back(fsdp::range_of(exp_avg, u->valid, 4, true, "exp_avg"));
-  ranges->push_back(fsdp::range_of(exp_avg_sq, u->valid, 4, true, "exp_avg_sq"));
-  if (w) ranges->push_back(fsdp::range_of(w, u->valid, 2, true, "param_bf16_out"));
+  ranges->push_back(fsdp::range_of(master, u->valid, 4, true, who + "master"));
+  ranges->push_back(fsdp::range_of(exp_avg, u->valid, 4, true, who + "exp_avg"));
+  ranges->push_back(fsdp::range_of(exp_avg_sq, u->valid, 4, true, who + "exp_avg_sq"));
+  if (w) ranges->push_back(fsdp::range_of(w, u->valid, 2, true, who + "param_bf16_out"));
   return FSDP_OK;
 }
 
@@ -779,6 +885,65 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
   a.s = to_device(hs);
   return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
                                 "fsdp_reduce_adamw_shard");
+}
+
+fsdp_status fsdp_reduce_adamw_units(int32_t n_units, const fsdp_unit_step* steps, int32_t n_grads,
+                                    const fsdp_adamw_hparams* hp, hipStream_t stream) {
+  fsdp::clear_error();
+  if (n_units < 0) return fail(FSDP_ERR_INVALID_ARG, "n_units must be >= 0 (got %d)", n_units);
+  if (n_units == 0) return FSDP_OK;
+  if (!steps) return fail(FSDP_ERR_INVALID_ARG, "steps array is NULL");
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
+  std::vector<StepArgs> args(static_cast<size_t>(n_units));
+  std::vector<fsdp::ByteRange> ranges;
+  for (int32_t i = 0; i < n_units; ++i) {
+    const fsdp_unit_step& st_i = steps[i];
+    const std::string who = "unit " + std::to_string(i) + " ";
+    if (!st_i.unit) return fail(FSDP_ERR_INVALID_ARG, "steps[%d].unit is NULL", i);
+    StepArgs& a = args[static_cast<size_t>(i)];
+    a = StepArgs{};
+    if (fsdp_status st = check_grads(st_i.unit, n_grads, st_i.grads, &ranges, &a, who)) return st;
+    if (fsdp_status st = check_state(st_i.unit, st_i.master, st_i.exp_avg, st_i.exp_avg_sq,
+                                     st_i.param_bf16_out, &ranges, &a, who))
+      return st;
+    a.n = st_i.unit->valid;
+    a.s = to_device(hs);
+  }
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  // aligned units go in batches through k_step_multi; the rest one by one
+  MultiArgs batch{};
+  auto flush = [&]() -> fsdp_status {
+    if (batch.nu == 0) return FSDP_OK;
+    batch.n_grads = n_grads;
+    batch.s = to_device(hs);
+    launch_multi(batch, stream);
+    batch = MultiArgs{};
+    return after_launch("fsdp_reduce_adamw_units");
+  };
+  for (int32_t i = 0; i < n_units; ++i) {
+    const StepArgs& a = args[static_cast<size_t>(i)];
+    if (a.n <= 0) continue;
+    if (n_grads > kMultiRows || a.n >= kBatchMaxElems ||
+        step_path(a, Op::Fused) != Path::Vector) {
+      if (fsdp_status st = launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
+                                                  "fsdp_reduce_adamw_units"))
+        return st;
+      continue;
+    }
+    UnitDesc& d = batch.u[batch.nu];
+    for (int k = 0; k < n_grads; ++k) d.g[k] = a.g[k];
+    d.p = a.p;
+    d.m = a.m;
+    d.v = a.v;
+    d.w = a.w;
+    d.n = a.n;
+    batch.tiles += (a.n + kStepTile - 1) / kStepTile;
+    d.tile_end = batch.tiles;
+    if (++batch.nu == kMaxMultiUnits)
+      if (fsdp_status st = flush()) return st;
+  }
+  return flush();
 }
 
 fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* const* tensors,

@@ -170,3 +170,27 @@ def test_status_strings(lib):
     raw = _raw(lib)
     assert raw.fsdp_status_string(0) == b"ok"
     assert raw.fsdp_status_string(3) == b"overlapping buffers"
+
+
+def test_multi_unit_step_validates_across_units(lib):
+    raw = _raw(lib)
+    u = lib.Unit([(4096,)], 8, 1)
+    rows0 = lib._ptr_array([FAKE + k * (1 << 20) for k in range(8)])
+    rows1 = lib._ptr_array([FAKE + (64 << 20) + k * (1 << 20) for k in range(8)])
+    base = FAKE + (1 << 30)
+
+    def step(rows, off):
+        return lib._UnitStep(u.handle.value, ctypes.cast(rows, ctypes.POINTER(ctypes.c_void_p)),
+                             base + off, base + off + (1 << 20), base + off + (2 << 20), None)
+
+    hp = ctypes.byref(_hp(lib))
+    arr = (lib._UnitStep * 2)(step(rows0, 0), step(rows1, 0))      # unit 1 master on unit 0's
+    assert raw.fsdp_reduce_adamw_units(2, arr, 8, hp, None) == 3
+    assert "unit 1 master overlaps unit 0 master" in raw.fsdp_last_error().decode()
+    arr = (lib._UnitStep * 2)(step(rows0, 0), step(rows0, 16 << 20))   # rows may be shared
+    arr[1].unit = None
+    assert raw.fsdp_reduce_adamw_units(2, arr, 8, hp, None) == 1
+    assert raw.fsdp_reduce_adamw_units(0, None, 8, hp, None) == 0
+    assert raw.fsdp_reduce_adamw_units(-1, None, 8, hp, None) == 1
+    arr = (lib._UnitStep * 1)(step(rows0, 0))
+    assert raw.fsdp_reduce_adamw_units(1, arr, 0, hp, None) == 1

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import datagen
 from datagen import workloads as W
 from shard_cases import ModelShard, assert_bf16_ulp, assert_rel, gather
 
@@ -28,14 +29,19 @@ import sharded_flatparameter_flatten_amd as fsdp  # noqa: E402
 HPD = fsdp.AdamWHparams(**W.ADAMW)
 
 
-def run_model(name, full_units, sparse_n):
+def run_model(name, full_units, sparse_n, multi=False):
     wl = W.WORKLOADS[name]
     ms = ModelShard(wl["units"], wl["F"], wl["rank"], wl["config"])
     units = [fsdp.Unit(W.shapes(u), wl["F"], wl["rank"]) for u in wl["units"]]
     assert [u.S for u in units] == [L.S for L in ms.L]
-    for i, u in enumerate(units):
-        fsdp.reduce_adamw_shard(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
-                                ms.window(ms.v, i), ms.window(ms.w, i), HPD, 1)
+    if multi:
+        fsdp.reduce_adamw_units([(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
+                                  ms.window(ms.v, i), ms.window(ms.w, i))
+                                 for i, u in enumerate(units)], HPD, 1)
+    else:
+        for i, u in enumerate(units):
+            fsdp.reduce_adamw_shard(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
+                                    ms.window(ms.v, i), ms.window(ms.w, i), HPD, 1)
     torch.cuda.synchronize()
     n_units = len(units)
     for i in range(n_units):
@@ -57,12 +63,43 @@ def run_model(name, full_units, sparse_n):
     return persistent
 
 
-def test_full_7b_rank_shard_every_unit():
-    assert run_model("full7b", {0, 15, 31}, 4096) == 13_476_831_232
+@pytest.mark.parametrize("multi", [False, True])
+def test_full_7b_rank_shard_every_unit(multi):
+    assert run_model("full7b", {0, 15, 31}, 4096, multi) == 13_476_831_232
 
 
 def test_full_70b_rank_shard_every_unit():
     free, total = torch.cuda.mem_get_info()
     if free < 170 * 2**30:
         pytest.skip(f"needs ~160 GB free HBM, {free / 2**30:.0f} GiB free")
-    assert run_model("full70b", {0, 40, 79}, 2048) == 137_953_296_384
+    assert run_model("full70b", {0, 40, 79}, 2048, multi=True) == 137_953_296_384
+
+
+@pytest.mark.parametrize("ng", [4, 8, 12])
+def test_multi_unit_step_equals_per_unit_calls(ng):
+    """Mixed list: aligned units (batched), shifted-row units, ng > 8 (one launch each)."""
+    from shard_cases import Case, assert_bits, to_np
+    specs = [([(300, 77)], 4, 1), ([(1000, 3), (17,)], 7, 1), ([(64, 64)], 2, 0),
+             ([(5,)], 8, 6), ([(2048 * 5 + 3,)], 3, 2)] * 7          # 35 units: > one batch
+    cases = [Case(sh, F, r, n_grads=ng, config=20 + j) for j, (sh, F, r) in enumerate(specs)]
+    ins = []
+    for j, c in enumerate(cases):
+        u = fsdp.Unit(c.shapes, c.F, c.rank)
+        p0 = torch.empty(u.S, dtype=torch.float32, device="cuda")
+        datagen.fill_normal_f32_(p0, c.master_seed, j, W.MASTER_SIGMA)
+        ins.append((u, c.device_grads(1), p0))
+    outs = {}
+    for mode in ("per_unit", "multi"):
+        st = [(u, g, p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0),
+               torch.empty(u.S, dtype=torch.bfloat16, device="cuda")) for u, g, p0 in ins]
+        if mode == "multi":
+            fsdp.reduce_adamw_units(st, HPD, 3)
+        else:
+            for s_ in st:
+                fsdp.reduce_adamw_shard(*s_, HPD, 3)
+        torch.cuda.synchronize()
+        outs[mode] = [[to_np(x)[:s_[0].shard_valid].copy() for x in s_[2:]] for s_ in st]
+    for a, b in zip(outs["per_unit"], outs["multi"]):
+        for x, y in zip(a, b):
+            assert_bits(x.view(np.uint32) if x.dtype == np.float32 else x,
+                        y.view(np.uint32) if y.dtype == np.float32 else y, "multi vs per-unit")
