@@ -13,5 +13,6 @@ from .fsdp_oracle import (  # noqa: F401
     persistent_bytes,
     reduce_adamw_shard,
     reduce_shard,
+    unflatten,
     unit_layout,
 )

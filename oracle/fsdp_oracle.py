@@ -27,7 +27,8 @@ the learning rate (decay applied as lr * wd * p).
 
 Parity status of each function (see the pins in tests/test_oracle_pins.py):
 ``unit_layout``, ``flatten_pad``, ``reduce_shard``, ``adamw_step``,
-``bf16_round_nearest_even``, ``cast_unflatten``, ``persistent_bytes`` are
+``bf16_round_nearest_even``, ``unflatten`` (bf16 and fp32 outputs), ``cast_unflatten``,
+``persistent_bytes`` are
 pinned. Parity unpinned: the choice of one binary32 op order among the
 mathematically equal ones (fixed by this file), and NaN payloads other than the
 canonical quiet NaN.
@@ -288,19 +289,22 @@ def reduce_adamw_shard(grads, layout: UnitLayout, p, m, v, hp: AdamW, step: int,
 # all-gather arithmetic + unflatten
 # ----------------------------------------------------------------------------
 
-def cast_unflatten(shards, layout: UnitLayout, shapes):
-    """Per-tensor bf16 outputs from the F rank shards of a unit.
+def unflatten(shards, layout: UnitLayout, shapes, out: str = "bf16"):
+    """Per-tensor outputs from the F rank shards of a unit.
 
     [FSDP-math, "The forward cycle: all-gather, compute, reshard"]: every rank
     contributes its slice and each ends with the unit's full weights, which
     the module then uses as ordinary per-tensor parameters.
-    [NOTE-003, "Key components"]: parameters travel in the low precision.
+    [Glossary, "Debugging FSDP" -> Checkpoint/Resume]: a full state dict
+    gathers the sharded state back into whole tensors (here in fp32 for the
+    master weights and the Adam moments).
 
     ``shards``: F arrays of S elements each (fp32 values, or uint16 bf16
     bits). Global element g of the unit lives in shard g // S at position
-    g % S. fp32 sources are rounded to bf16 (nearest, ties to even); bf16
-    sources are copied bit for bit. Pad slots are never read.
-    Returns a list of uint16 arrays shaped like ``shapes``.
+    g % S; pad slots are never read. ``out``: "bf16" (fp32 sources rounded to
+    nearest even, bf16 sources copied bit for bit) or "f32" (fp32 sources
+    copied bit for bit, bf16 sources widened exactly).
+    Returns a list of arrays shaped like ``shapes`` (uint16 bits or float32).
     """
     S = layout.S
     outs = []
@@ -314,11 +318,18 @@ def cast_unflatten(shards, layout: UnitLayout, shapes):
         for shard_id in np.unique(k):
             sel = k == shard_id
             vals[sel] = np.asarray(shards[int(shard_id)])[local[sel]]
-        if src_dtype == np.float32:
-            bits = bf16_round_nearest_even(vals)
-        elif src_dtype == np.uint16:
-            bits = vals
-        else:
+        if src_dtype not in (np.float32, np.uint16):
             raise TypeError("shards must be float32 values or uint16 bf16 bits")
-        outs.append(bits.reshape(tuple(shape)))
+        if out == "bf16":
+            res = bf16_round_nearest_even(vals) if src_dtype == np.float32 else vals
+        elif out == "f32":
+            res = vals if src_dtype == np.float32 else bf16_widen(vals)
+        else:
+            raise ValueError("out must be 'bf16' or 'f32'")
+        outs.append(res.reshape(tuple(shape)))
     return outs
+
+
+def cast_unflatten(shards, layout: UnitLayout, shapes):
+    """The all-gather arithmetic: ``unflatten`` into bf16 parameters."""
+    return unflatten(shards, layout, shapes, out="bf16")

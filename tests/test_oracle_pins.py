@@ -208,6 +208,42 @@ def test_unflatten_from_fp32_matches_torch_cast():
         assert out.shape == s
 
 
+@pytest.mark.parametrize("F", [1, 3, 8])
+def test_state_dict_export_resume_round_trip(F):
+    """fp32 shards -> per-tensor fp32 (export) -> flatten into shards (resume): identity."""
+    rng = np.random.default_rng(10 + F)
+    shapes = [(37, 5), (11,), (64, 3)]
+    U = sum(O.numel(s) for s in shapes)
+    S = -(-U // F)
+    flat = rng.standard_normal(F * S).astype(np.float32)
+    flat[U:] = 0.0
+    shards = [flat[r * S:(r + 1) * S].copy() for r in range(F)]
+    L = O.unit_layout(shapes, F, 0)
+    tensors = O.unflatten(shards, L, shapes, out="f32")
+    # library pin: the export is the flat buffer split by numpy at the tensor offsets
+    pieces = np.split(flat[:U], np.cumsum([O.numel(s) for s in shapes])[:-1])
+    for t, piece, s in zip(tensors, pieces, shapes):
+        assert t.shape == s and np.array_equal(t.reshape(-1).view(np.uint32), piece.view(np.uint32))
+    back = [O.flatten_pad([t.view(np.uint32) for t in tensors], F, r * S, S).view(np.float32)
+            for r in range(F)]
+    for a, b in zip(back, shards):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_unflatten_bf16_to_f32_widens_exactly():
+    rng = np.random.default_rng(12)
+    shapes = [(9, 7), (5,)]
+    L = O.unit_layout(shapes, 4, 0)
+    shards = [rng.integers(0, 1 << 16, L.S, dtype=np.uint64).astype(np.uint16) for _ in range(4)]
+    outs = O.unflatten(shards, L, shapes, out="f32")
+    flat = np.concatenate(shards)[:L.U]
+    ref = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got = np.concatenate([o.reshape(-1) for o in outs])
+    nan = np.isnan(ref)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.all(np.isnan(got[nan]))
+
+
 # ----------------------------------------------------------------------------
 # reduce-scatter arithmetic
 # ----------------------------------------------------------------------------
