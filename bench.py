@@ -270,6 +270,65 @@ def sharding_sweep(args):
                       "rows": out}), flush=True)
 
 
+def state_dict_bench(args):
+    """Full-state-dict export (F fp32 shards -> whole fp32 tensors, for master, m and v)
+    and resume (whole tensors -> this rank's fp32 shard) on the 7B block at F=8."""
+    import torch
+
+    import datagen
+    import sharded_flatparameter_flatten_amd as fsdp
+    from datagen import workloads as W
+
+    dev = torch.device("cuda:0")
+    shapes, F = W.shapes(W.BLK7), 8
+    units = [fsdp.Unit(shapes, F, r) for r in range(F)]
+    U, S = units[0].U, units[0].S
+    R = args.rotate
+    sets = []
+    for j in range(R):
+        shards = []
+        for kind in range(3):
+            row = []
+            for r in range(F):
+                t = torch.empty(S, dtype=torch.float32, device=dev)
+                datagen.fill_normal_f32_(t, datagen.seed_for(16, 0), 100 * j + 10 * kind + r, 0.02)
+                row.append(t)
+            shards.append(row)
+        whole = [[torch.empty(sh, dtype=torch.float32, device=dev) for sh in shapes]
+                 for _ in range(3)]
+        back = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(3)]
+        sets.append((shards, whole, back))
+    stream = torch.cuda.current_stream(dev)
+
+    def export(i):
+        shards, whole, _ = sets[i % R]
+        for kind in range(3):
+            fsdp.unflatten(units[0], shards[kind], whole[kind], stream=stream)
+
+    def resume(i):
+        _, whole, back = sets[i % R]
+        for kind in range(3):
+            fsdp.flatten_pad(units[0], whole[kind], back[kind], stream=stream)
+
+    res = {}
+    for name, fn, nbytes in (("export", export, 3 * 8 * U), ("resume", resume, 3 * 8 * S)):
+        for i in range(max(args.warmup, R)):
+            fn(i)
+        K = max(args.steps, 2 * R)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                     "frac_of_8TBps": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+    print(json.dumps({"metric": "full-state-dict export/resume (fp32 master, m, v)",
+                      "workload": "7B block unit, F=8, rank 0", "rotating_sets": R, **res}),
+          flush=True)
+
+
 def _counter_rows(path):
     import csv
     import glob
@@ -348,7 +407,7 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
-    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep"])
+    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict"])
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -373,6 +432,9 @@ def main():
         sys.exit(1)
     if args.workload == "sweep":
         sharding_sweep(args)
+        return
+    if args.workload == "state_dict":
+        state_dict_bench(args)
         return
     if args.workload != "blk7":
         model_sequence(args)

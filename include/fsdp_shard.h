@@ -213,6 +213,20 @@ fsdp_status fsdp_cast_unflatten(const fsdp_unit* unit, fsdp_dtype src_dtype,
                                 const void* const* shards, void* const* tensors_bf16,
                                 hipStream_t stream);
 
+/* Unflatten with any element type on either side: fsdp_cast_unflatten with a
+ * chosen output dtype. FSDP_F32 -> FSDP_F32 and FSDP_BF16 -> FSDP_BF16 copy
+ * bits; FSDP_F32 -> FSDP_BF16 rounds to nearest even (NaN -> 0x7FC0);
+ * FSDP_BF16 -> FSDP_F32 widens exactly. With fp32 on both sides this is the
+ * export half of a full state dict: the F shards of master, exp_avg or
+ * exp_avg_sq become whole per-tensor fp32 tensors ([Glossary, "Debugging
+ * FSDP" -> Checkpoint/Resume]); fsdp_flatten_pad with FSDP_F32 is the resume
+ * half. `tensors`: host array of T device pointers, tensor i receiving n_i
+ * elements of dst_dtype. Shards holding only pad are not read (their pointer
+ * may be NULL). */
+fsdp_status fsdp_unflatten(const fsdp_unit* unit, fsdp_dtype src_dtype, fsdp_dtype dst_dtype,
+                           const void* const* shards, void* const* tensors,
+                           hipStream_t stream);
+
 const char* fsdp_status_string(fsdp_status status);
 const char* fsdp_last_error(void);
 

@@ -15,7 +15,8 @@ Names follow the C ABI in include/fsdp_shard.h:
 * ``reduce_adamw_shard(unit, grads, master, exp_avg, exp_avg_sq, param_out, hp)``
                                             -> fsdp_reduce_adamw_shard
 * ``reduce_adamw_units(steps, hp, step)``   -> fsdp_reduce_adamw_units
-* ``cast_unflatten(unit, shards, outs)``    -> fsdp_cast_unflatten
+* ``cast_unflatten(unit, shards, outs)``    -> fsdp_cast_unflatten (bf16 outputs)
+* ``unflatten(unit, shards, outs)``         -> fsdp_unflatten (dtypes from the tensors)
 """
 
 from __future__ import annotations
@@ -28,7 +29,7 @@ import torch
 
 __all__ = [
     "FsdpError", "Unit", "AdamWHparams", "flatten_pad", "reduce_shard", "adamw_shard",
-    "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "abi_version", "library_path",
+    "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "unflatten", "abi_version", "library_path",
     "F32", "BF16",
 ]
 
@@ -99,6 +100,7 @@ def _load():
         "fsdp_cast_unflatten": (st, [vp, st, _c_void_p_p, _c_void_p_p, vp]),
         "fsdp_reduce_adamw_units": (st, [i32, ctypes.POINTER(_UnitStep), i32,
                                          ctypes.POINTER(_Hparams), vp]),
+        "fsdp_unflatten": (st, [vp, st, st, _c_void_p_p, _c_void_p_p, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -301,20 +303,27 @@ def reduce_adamw_units(steps, hp: AdamWHparams, step: int, grad_scale: float | N
         UnitsStep(steps)(hp, step, grad_scale, stream)
 
 
-def cast_unflatten(unit: Unit, shards, outs, stream=None):
+def unflatten(unit: Unit, shards, outs, stream=None):
+    """Per-tensor outputs from the F shards; element types from the tensors (fp32/bf16)."""
     if len(shards) != unit.F:
         raise ValueError(f"need {unit.F} shards, got {len(shards)}")
     if len(outs) != unit.n_tensors:
         raise ValueError(f"need {unit.n_tensors} outputs, got {len(outs)}")
-    sdtype = shards[0].dtype
-    if sdtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("shards must be float32 or bfloat16")
-    code = F32 if sdtype == torch.float32 else BF16
+    sdtype, ddtype = shards[0].dtype, outs[0].dtype
+    codes = {torch.float32: F32, torch.bfloat16: BF16}
+    if sdtype not in codes or ddtype not in codes:
+        raise TypeError("shards and outputs must be float32 or bfloat16")
     sp = []
     for k, s in enumerate(shards):
         valid = max(0, min(unit.S, unit.U - k * unit.S))
         sp.append(_dev(s, sdtype, f"shards[{k}]", valid))
-    op = [_dev(o, torch.bfloat16, f"outs[{i}]", n) for i, (o, n) in
-          enumerate(zip(outs, unit.numels))]
-    _check(_lib.fsdp_cast_unflatten(unit.handle, code, _ptr_array(sp), _ptr_array(op),
-                                    _stream(stream, outs[0].device)))
+    op = [_dev(o, ddtype, f"outs[{i}]", n) for i, (o, n) in enumerate(zip(outs, unit.numels))]
+    _check(_lib.fsdp_unflatten(unit.handle, codes[sdtype], codes[ddtype], _ptr_array(sp),
+                               _ptr_array(op), _stream(stream, outs[0].device)))
+
+
+def cast_unflatten(unit: Unit, shards, outs, stream=None):
+    """The all-gather arithmetic: F shards -> per-tensor bf16 parameters."""
+    if outs and outs[0].dtype != torch.bfloat16:
+        raise TypeError("cast_unflatten writes bf16 tensors; use unflatten for fp32 outputs")
+    unflatten(unit, shards, outs, stream)

@@ -515,10 +515,11 @@ struct SegArgs {
   int32_t pad_;
 };
 
-// KIND 0: 4-byte bit copy; 1: 2-byte bit copy; 2: fp32 -> bf16 (nearest even).
-// A lane moves EPL consecutive elements: exactly one 16-byte source vector,
-// so every load (and store) instruction of a wavefront is one contiguous
-// range and no cache line is written in pieces by different instructions.
+// KIND 0: 4-byte bit copy; 1: 2-byte bit copy; 2: fp32 -> bf16 (nearest even);
+// 3: bf16 -> fp32 (exact). A lane moves EPL consecutive elements: one 16-byte
+// source vector (8 bytes for KIND 3, whose 16-byte store is the wider side),
+// so every load and store instruction of a wavefront is one contiguous range
+// and no cache line is written in pieces by different instructions.
 template <int KIND>
 struct CopyKind;
 template <>
@@ -554,6 +555,21 @@ struct CopyKind<2> {
     st<u32x2, kCopyNt>(d, u32x2{pack_bf16(x.x, x.y), pack_bf16(x.z, x.w)});
   }
   static __device__ __forceinline__ void zero(D* d) { st<u32x2, kCopyNt>(d, u32x2{0u, 0u}); }
+};
+
+template <>
+struct CopyKind<3> {
+  using S = uint16_t;
+  using D = float;
+  static constexpr int EPL = 4;
+  static __device__ __forceinline__ D cvt(S x) { return widen(x); }
+  static __device__ __forceinline__ void vec(const S* s, D* d) {
+    const u32x2 q = ldh<u32x2, kCopyNtLoad>(s);
+    st<f32x4, kCopyNt>(d, f32x4{lo_bf16(q.x), hi_bf16(q.x), lo_bf16(q.y), hi_bf16(q.y)});
+  }
+  static __device__ __forceinline__ void zero(D* d) {
+    st<f32x4, kCopyNt>(d, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
 };
 
 // Elements per lane, and per workgroup tile, of each copy kind (host and device).
@@ -683,14 +699,15 @@ struct Piece {
 };
 
 // Splits each piece into an unaligned scalar head and an aligned vector body
-// (source on 16 bytes, destination on one lane's store width) when some head
+// (each side on one lane's access width) when some head
 // length h < EPL aligns both sides; otherwise the whole piece is scalar. Then
 // launches the segments in batches of kMaxSeg.
 fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_t stream,
                           const char* what) {
-  const int64_t ss = kind == 1 ? 2 : 4;      // source element bytes
-  const int64_t ds = kind == 0 ? 4 : 2;      // destination element bytes
+  const int64_t ss = (kind == 1 || kind == 3) ? 2 : 4;   // source element bytes
+  const int64_t ds = (kind == 0 || kind == 3) ? 4 : 2;   // destination element bytes
   const int64_t epl = copy_epl(kind);
+  const uintptr_t smask = uintptr_t(epl * ss - 1);
   const uintptr_t dmask = uintptr_t(epl * ds - 1);
   std::vector<Seg> segs;
   segs.reserve(pieces.size() * 2);
@@ -700,7 +717,7 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(pc.dst);
     int64_t head = -1;
     for (int64_t h = 0; h < epl && h < pc.len; ++h) {
-      const bool s_ok = pc.src == nullptr || ((s0 + h * ss) & 15u) == 0;
+      const bool s_ok = pc.src == nullptr || ((s0 + h * ss) & smask) == 0;
       const bool d_ok = ((d0 + h * ds) & dmask) == 0;
       if (s_ok && d_ok) { head = h; break; }
     }
@@ -730,7 +747,8 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     switch (kind) {
       case 0: k_segcopy<0><<<grid, kThreads, 0, stream>>>(a); break;
       case 1: k_segcopy<1><<<grid, kThreads, 0, stream>>>(a); break;
-      default: k_segcopy<2><<<grid, kThreads, 0, stream>>>(a); break;
+      case 2: k_segcopy<2><<<grid, kThreads, 0, stream>>>(a); break;
+      default: k_segcopy<3><<<grid, kThreads, 0, stream>>>(a); break;
     }
     if (fsdp_status st = after_launch(what)) return st;
   }
@@ -985,42 +1003,52 @@ fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* c
   return launch_pieces(pieces, dtype == FSDP_F32 ? 0 : 1, stream, "fsdp_flatten_pad");
 }
 
-fsdp_status fsdp_cast_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype,
-                                const void* const* shards, void* const* tensors_bf16,
-                                hipStream_t stream) {
+fsdp_status fsdp_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype, fsdp_dtype dst_dtype,
+                           const void* const* shards, void* const* tensors, hipStream_t stream) {
   fsdp::clear_error();
   if (fsdp_status st = fsdp::check_unit(u)) return st;
-  if (src_dtype != FSDP_F32 && src_dtype != FSDP_BF16)
-    return fail(FSDP_ERR_UNSUPPORTED, "dtype %d not supported", static_cast<int>(src_dtype));
+  if ((src_dtype != FSDP_F32 && src_dtype != FSDP_BF16) ||
+      (dst_dtype != FSDP_F32 && dst_dtype != FSDP_BF16))
+    return fail(FSDP_ERR_UNSUPPORTED, "dtype pair (%d, %d) not supported",
+                static_cast<int>(src_dtype), static_cast<int>(dst_dtype));
   if (!shards) return fail(FSDP_ERR_INVALID_ARG, "shards array is NULL");
-  if (!tensors_bf16) return fail(FSDP_ERR_INVALID_ARG, "tensors array is NULL");
+  if (!tensors) return fail(FSDP_ERR_INVALID_ARG, "tensors array is NULL");
   const int64_t ss = src_dtype == FSDP_F32 ? 4 : 2;
+  const int64_t ds = dst_dtype == FSDP_F32 ? 4 : 2;
+  const int kind = src_dtype == dst_dtype ? (ss == 4 ? 0 : 1) : (src_dtype == FSDP_F32 ? 2 : 3);
   std::vector<Piece> pieces;
   std::vector<fsdp::ByteRange> ranges;
   for (int32_t k = 0; k < u->F; ++k) {
+    const int64_t kv = std::max<int64_t>(0, std::min<int64_t>(u->S, u->U - k * u->S));
+    if (kv == 0) continue;                 // a shard holding only pad is never read
     if (!shards[k]) return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is NULL", k);
     if (reinterpret_cast<uintptr_t>(shards[k]) % ss)
       return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is not element aligned", k);
-    const int64_t kv = std::max<int64_t>(0, std::min<int64_t>(u->S, u->U - k * u->S));
     ranges.push_back(fsdp::range_of(shards[k], kv, ss, false, "shards[" + std::to_string(k) + "]"));
   }
   for (int32_t i = 0; i < u->T; ++i) {
     if (u->numel[i] == 0) continue;
-    if (!tensors_bf16[i]) return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is NULL", i);
-    if (reinterpret_cast<uintptr_t>(tensors_bf16[i]) & 1u)
-      return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is not 2-byte aligned", i);
-    ranges.push_back(fsdp::range_of(tensors_bf16[i], u->numel[i], 2, true,
+    if (!tensors[i]) return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is NULL", i);
+    if (reinterpret_cast<uintptr_t>(tensors[i]) % ds)
+      return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is not element aligned", i);
+    ranges.push_back(fsdp::range_of(tensors[i], u->numel[i], ds, true,
                                     "tensors[" + std::to_string(i) + "]"));
     const int64_t lo = u->offset[i], hi = u->offset[i + 1];
     for (int64_t k = lo / u->S; k * u->S < hi; ++k) {
       const int64_t a = std::max(lo, k * u->S);
       const int64_t b = std::min(hi, (k + 1) * u->S);
       pieces.push_back(Piece{static_cast<const char*>(shards[k]) + (a - k * u->S) * ss,
-                             static_cast<char*>(tensors_bf16[i]) + (a - lo) * 2, b - a});
+                             static_cast<char*>(tensors[i]) + (a - lo) * ds, b - a});
     }
   }
   if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  return launch_pieces(pieces, src_dtype == FSDP_F32 ? 2 : 1, stream, "fsdp_cast_unflatten");
+  return launch_pieces(pieces, kind, stream, "fsdp_unflatten");
+}
+
+fsdp_status fsdp_cast_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype,
+                                const void* const* shards, void* const* tensors_bf16,
+                                hipStream_t stream) {
+  return fsdp_unflatten(u, src_dtype, FSDP_BF16, shards, tensors_bf16, stream);
 }
 
 }  // extern "C"
