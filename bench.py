@@ -77,19 +77,32 @@ def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
     v = np.zeros(n, np.float32)
     one = O.unit_layout([(n,)], 1, 0)
     hp = O.AdamW(**W.ADAMW)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.reduce_adamw_shard(grads, one, p, m, v, hp, 1, grad_scale=1.0 / F, emit_bf16=True)
-        reps += 1
-        el = time.perf_counter() - t0
-        if reps >= 3 and el >= budget_s:
-            break
+
+    def rate(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if reps >= 3 and el >= budget:
+                return n * reps / el, reps, el
+
+    value, reps, el = rate(lambda: O.reduce_adamw_shard(grads, one, p, m, v, hp, 1,
+                                                        grad_scale=1.0 / F, emit_bf16=True),
+                           budget_s)
+    g = O.reduce_shard(grads, one, grad_scale=1.0 / F)
+    rows = {
+        "a3_reduce_shard": rate(lambda: O.reduce_shard(grads, one, grad_scale=1.0 / F), 2.0)[0],
+        "a4_adamw_shard_emit": rate(lambda: O.adamw_step(g, p, m, v, hp, 1, emit_bf16=True),
+                                    2.0)[0],
+        "a6_bf16_round": rate(lambda: O.bf16_round_nearest_even(p), 2.0)[0],
+    }
     return {
-        "value": n * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+        "value": value, "unit": "params/s", "cores": 1, "kind": "oracle",
         "sample": (f"fused reduce+AdamW+bf16 emit of the CPU oracle (numpy, one thread) on the "
                    f"first {n:,} elements of rank {rank}'s shard of the 7B block at F={F}, "
                    f"{reps} repetitions, {el:.1f} s"),
+        "rows_params_per_s": rows,
     }
 
 
@@ -453,7 +466,7 @@ def main():
     # (every set has its own gradient windows, optimizer state, bf16 shards and
     # outputs, so no step finds the previous step's data in a cache)
     row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1))
-    sets = []
+    sets, set_masters = [], []
     for j in range(R):
         masters = []
         for i, nel in enumerate(u.numels):
@@ -468,11 +481,12 @@ def main():
             sh = torch.empty(S, dtype=torch.bfloat16, device=dev)
             fsdp.flatten_pad(units[r], masters_bf16, sh)
             shards.append(sh)
-        del masters, masters_bf16
+        del masters_bf16
         m = torch.zeros(S, dtype=torch.float32, device=dev)
         v = torch.zeros(S, dtype=torch.float32, device=dev)
         outs = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes]
         sets.append((row_sets[j], p, m, v, shards, outs))
+        set_masters.append(masters)
     hp = fsdp.AdamWHparams(**W.ADAMW)
     torch.cuda.synchronize()
 
@@ -511,6 +525,45 @@ def main():
     fused_avg = sum(fused_ms) / K
     gather_avg = sum(gather_ms) / K
     ms_per_step = elapsed * 1e3 / K
+
+    # ---- every row of the path on its own (same rotation) -----------------
+    g32 = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(R)]
+    flat_dst = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def timed(fn, reps):
+        for i in range(R):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def row(name, us, nbytes):
+        return {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                "frac_of_8TBps": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+
+    reps = max(2 * R, args.steps // 2)
+    rows = {
+        "a2_flatten_pad_fp32": row("flatten", timed(lambda i: fsdp.flatten_pad(
+            u, set_masters[i % R], flat_dst[i % R], stream=stream), reps), 8 * S),
+        "a3_reduce_shard": row("reduce", timed(lambda i: fsdp.reduce_shard(
+            u, sets[i % R][0], g32[i % R], stream=stream), reps), (2 * F + 4) * n),
+        "a4_adamw_shard_emit": row("adamw", timed(lambda i: fsdp.adamw_shard(
+            u, g32[i % R], sets[i % R][1], sets[i % R][2], sets[i % R][3], sets[i % R][4][rank],
+            hp, 2, stream=stream), reps), 30 * n),
+        "a5_fused_no_emit": row("fused", timed(lambda i: fsdp.reduce_adamw_shard(
+            u, sets[i % R][0], sets[i % R][1], sets[i % R][2], sets[i % R][3], None, hp, 2,
+            stream=stream), reps), (2 * F + 24) * n),
+        "a5_fused_emit": row("fused", timed(lambda i: fsdp.reduce_adamw_shard(
+            u, sets[i % R][0], sets[i % R][1], sets[i % R][2], sets[i % R][3],
+            sets[i % R][4][rank], hp, 2, stream=stream), reps), (2 * F + 26) * n),
+        "a6_cast_unflatten_bf16": row("gather", timed(lambda i: fsdp.cast_unflatten(
+            u, sets[i % R][4], sets[i % R][5], stream=stream), reps), 4 * u.U),
+    }
+    del g32, flat_dst, set_masters
 
     # ---- reference: the library's plain 4-byte copy of 1 GiB (same run) ----
     # (one tensor, F = 1: fsdp_flatten_pad is then a straight copy; its
@@ -559,6 +612,7 @@ def main():
         "step_GBps": (fused_bytes + gather_bytes) / (ms_per_step * 1e-3) / 1e9,
         "unit_params_per_s": u.U / (ms_per_step * 1e-3),
         "copy_GBps": copy_gbps,
+        "rows_alone": rows,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
