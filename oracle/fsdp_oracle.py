@@ -28,7 +28,7 @@ the learning rate (decay applied as lr * wd * p).
 Parity status of each function (see the pins in tests/test_oracle_pins.py):
 ``unit_layout``, ``flatten_pad``, ``reduce_shard``, ``adamw_step``,
 ``bf16_round_nearest_even``, ``unflatten`` (bf16 and fp32 outputs), ``cast_unflatten``,
-``persistent_bytes`` are
+``reduce_shard_hybrid``, ``persistent_bytes`` are
 pinned. Parity unpinned: the choice of one binary32 op order among the
 mathematically equal ones (fixed by this file), and NaN payloads other than the
 canonical quiet NaN.
@@ -197,6 +197,44 @@ def reduce_shard(grads, layout: UnitLayout, grad_scale: float | None = None) -> 
     for k in range(1, n):
         acc = acc + bf16_widen(grads[k][lo:hi])
     return acc * gs
+
+
+def reduce_shard_hybrid(grads, layout: UnitLayout, replicas: int,
+                        grad_scale: float | None = None) -> np.ndarray:
+    """Hybrid sharding: this rank's slice of the gradient summed over R groups of F ranks.
+
+    [NOTE-003, "Concepts"]: hybrid sharding shards within a group and
+    replicates across groups. [Glossary, "Hybrid Sharding"]: gradients are
+    all-reduced across the replica groups (data-parallel style) and sharded
+    within a group. Reading: ``grads`` holds R*F rows, replica-major (row
+    rho*F + f is rank f of group rho, F = layout.F); each group first sums its
+    F rows in rank order (the reduce-scatter inside the group, a left fold
+    from rank 0's value), then the R group sums are added in group order (the
+    all-reduce across groups, again a left fold), then scaled by
+    fp32(grad_scale), default 1/(R*F) computed in double.
+    """
+    F = layout.F
+    if replicas < 1 or len(grads) != replicas * F:
+        raise ValueError("need replicas * F gradient rows")
+    if grad_scale is None:
+        grad_scale = 1.0 / (replicas * F)
+    gs = np.float32(grad_scale)
+    lo = layout.shard_begin
+    hi = lo + layout.shard_valid
+    total = None
+    for rho in range(replicas):
+        group = bf16_widen(grads[rho * F][lo:hi])
+        for f in range(1, F):
+            group = group + bf16_widen(grads[rho * F + f][lo:hi])
+        total = group if total is None else total + group
+    return total * gs
+
+
+def reduce_adamw_shard_hybrid(grads, layout: UnitLayout, replicas: int, p, m, v, hp, step: int,
+                              grad_scale: float | None = None, emit_bf16: bool = False):
+    """The hybrid reduction followed by ``adamw_step`` on its fp32 result."""
+    g = reduce_shard_hybrid(grads, layout, replicas, grad_scale)
+    return adamw_step(g, p, m, v, hp, step, emit_bf16)
 
 
 # ----------------------------------------------------------------------------

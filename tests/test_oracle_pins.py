@@ -331,6 +331,46 @@ def test_reduce_brute_force_fractions_tiny():
             assert abs(Fraction(float(got[e])) - exact) <= gamma * mag
 
 
+def test_hybrid_reduce_special_cases_reduce_to_the_flat_fold():
+    shapes = [(777,)]
+    rows8 = [rng_bf16(101, 777, 1e-3, k) for k in range(8)]
+    # one replica group: the plain F-way reduction
+    L8 = O.unit_layout(shapes, 8, 3)
+    assert np.array_equal(O.reduce_shard_hybrid(rows8, L8, 1), O.reduce_shard(rows8, L8))
+    # groups of one rank (F = 1): the plain fold over the R replicas
+    L1 = O.unit_layout(shapes, 1, 0)
+    assert np.array_equal(O.reduce_shard_hybrid(rows8, L1, 8), O.reduce_shard(rows8, L1))
+
+
+def test_hybrid_reduce_two_by_two_closed_form():
+    """R = 2 groups of F = 2: fl(fl(a+b) + fl(c+d)), each pair sum one rounding of the exact sum."""
+    n = 1 << 14
+    rows = [rng_bf16(111, n, 1e-3, k) for k in range(4)]
+    rows[2][:128] = rng_bf16(112, 128, 1e-9, 0)            # wide exponent gaps: rounding happens
+    L = O.unit_layout([(2 * n,)], 2, 0)                     # rank 0 of F = 2: elements [0, n)
+    rows = [np.concatenate([r, r]) for r in rows]
+    got = O.reduce_shard_hybrid(rows, L, 2, grad_scale=1.0)
+    x = [O.bf16_widen(r[:n]).astype(np.float64) for r in rows]
+    g0 = (x[0] + x[1]).astype(np.float32).astype(np.float64)   # exact pair sum, rounded once
+    g1 = (x[2] + x[3]).astype(np.float32).astype(np.float64)
+    want = (g0 + g1).astype(np.float32)
+    assert np.array_equal(got, want)
+    flat = O.reduce_shard(rows, O.unit_layout([(2 * n,)], 2, 0), grad_scale=1.0)
+    assert not np.array_equal(got, flat)                    # the two trees round differently
+
+
+def test_hybrid_reduce_within_summation_bound():
+    n, R, F = 1 << 13, 4, 4
+    rows = [datagen.bf16_bits_host(datagen.seed_for(3, 1), k, np.arange(n * F), 1e-3,
+                                   outlier_seed=datagen.seed_for(3, 2)) for k in range(R * F)]
+    L = O.unit_layout([(n * F,)], F, 1)
+    got = O.reduce_shard_hybrid(rows, L, R, grad_scale=1.0).astype(np.float64)
+    vals = np.stack([O.bf16_widen(r[n:2 * n]).astype(np.float64) for r in rows])
+    depth = (F - 1) + (R - 1)
+    gamma = depth * U32 / (1 - depth * U32)
+    assert np.all(np.abs(got - vals.sum(axis=0)) <= gamma * np.abs(vals).sum(axis=0))
+
+
 # ----------------------------------------------------------------------------
 # AdamW
 # ----------------------------------------------------------------------------
