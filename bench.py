@@ -283,6 +283,50 @@ def sharding_sweep(args):
                       "rows": out}), flush=True)
 
 
+def hybrid_bench(args):
+    """Hybrid sharding on the 7B block: R = 2 replica groups of F = 8, rank 0, fused step."""
+    import torch
+
+    import datagen
+    import sharded_flatparameter_flatten_amd as fsdp
+    from datagen import workloads as W
+
+    dev = torch.device("cuda:0")
+    shapes, F, Rg, rank = W.shapes(W.BLK7), 8, 2, 0
+    u = fsdp.Unit(shapes, F, rank)
+    R = args.rotate
+    rows = rotating_rows(torch, datagen, W, u, Rg * F, R, dev, datagen.seed_for(17, 1, 1))
+    state = []
+    for j in range(R):
+        p = torch.empty(u.S, dtype=torch.float32, device=dev)
+        datagen.fill_normal_f32_(p, datagen.seed_for(17, 0), j, W.MASTER_SIGMA)
+        state.append((p, torch.zeros_like(p), torch.zeros_like(p),
+                      torch.empty(u.S, dtype=torch.bfloat16, device=dev)))
+    hp = fsdp.AdamWHparams(**W.ADAMW)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn in (("hybrid", lambda i: fsdp.reduce_adamw_shard_hybrid(
+                          u, Rg, rows[i % R], *state[i % R], hp, 2, stream=stream)),
+                     ("flat_16_rows", lambda i: fsdp.reduce_adamw_shard(
+                          u, rows[i % R], *state[i % R], hp, 2, stream=stream))):
+        for i in range(max(args.warmup, R)):
+            fn(i)
+        K = max(args.steps, 2 * R)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        nbytes = (2 * Rg * F + 26) * u.shard_valid
+        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                     "frac_of_8TBps": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+    print(json.dumps({"metric": "hybrid-sharding fused shard step (2 groups x F=8)",
+                      "workload": "7B block unit, F=8, 2 replica groups, rank 0",
+                      "rotating_sets": R, **res}), flush=True)
+
+
 def state_dict_bench(args):
     """Full-state-dict export (F fp32 shards -> whole fp32 tensors, for master, m and v)
     and resume (whole tensors -> this rank's fp32 shard) on the 7B block at F=8."""
@@ -420,7 +464,7 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
-    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict"])
+    ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -448,6 +492,9 @@ def main():
         return
     if args.workload == "state_dict":
         state_dict_bench(args)
+        return
+    if args.workload == "hybrid":
+        hybrid_bench(args)
         return
     if args.workload != "blk7":
         model_sequence(args)

@@ -172,6 +172,27 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* unit, int32_t n_grads,
                                     void* param_bf16_out,
                                     const fsdp_adamw_hparams* hp, hipStream_t stream);
 
+/* Hybrid sharding (HSDP): the unit is sharded F ways inside each of `replicas`
+ * (R) groups and replicated across groups. [NOTE-003, "Concepts"]: shard within
+ * a group, replicate across groups; [Glossary, "Hybrid Sharding"]: gradients
+ * are all-reduced across the groups and sharded within a group.
+ * `grads`: host array of R*F device pointers, replica-major: row rho*F + f is
+ * rank f of group rho, each the full bf16 unit gradient (U elements). For
+ * i < shard_valid: each group left-folds its F rows in rank order in fp32
+ * (the reduce-scatter inside the group), the R group sums are left-folded in
+ * group order (the all-reduce across groups) and the result is multiplied by
+ * fp32(grad_scale) (1/(R*F) gives the mean). R = 1 is fsdp_reduce_shard.
+ * Requires 1 <= R*F <= 64. Same buffers and rules as the flat entry points. */
+fsdp_status fsdp_reduce_shard_hybrid(const fsdp_unit* unit, int32_t replicas,
+                                     const void* const* grads, double grad_scale, float* out,
+                                     hipStream_t stream);
+/* The hybrid reduction followed by AdamW in one pass, as fsdp_reduce_adamw_shard. */
+fsdp_status fsdp_reduce_adamw_shard_hybrid(const fsdp_unit* unit, int32_t replicas,
+                                           const void* const* grads, float* master,
+                                           float* exp_avg, float* exp_avg_sq,
+                                           void* param_bf16_out,
+                                           const fsdp_adamw_hparams* hp, hipStream_t stream);
+
 /* One unit's share of a multi-unit optimizer step (see fsdp_reduce_adamw_units). */
 typedef struct {
   const fsdp_unit* unit;

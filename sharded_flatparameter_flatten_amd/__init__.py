@@ -15,6 +15,7 @@ Names follow the C ABI in include/fsdp_shard.h:
 * ``reduce_adamw_shard(unit, grads, master, exp_avg, exp_avg_sq, param_out, hp)``
                                             -> fsdp_reduce_adamw_shard
 * ``reduce_adamw_units(steps, hp, step)``   -> fsdp_reduce_adamw_units
+* ``reduce_shard_hybrid`` / ``reduce_adamw_shard_hybrid`` -> the hybrid-sharding forms
 * ``cast_unflatten(unit, shards, outs)``    -> fsdp_cast_unflatten (bf16 outputs)
 * ``unflatten(unit, shards, outs)``         -> fsdp_unflatten (dtypes from the tensors)
 """
@@ -29,7 +30,8 @@ import torch
 
 __all__ = [
     "FsdpError", "Unit", "AdamWHparams", "flatten_pad", "reduce_shard", "adamw_shard",
-    "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "unflatten", "abi_version", "library_path",
+    "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "unflatten",
+    "reduce_shard_hybrid", "reduce_adamw_shard_hybrid", "abi_version", "library_path",
     "F32", "BF16",
 ]
 
@@ -101,6 +103,9 @@ def _load():
         "fsdp_reduce_adamw_units": (st, [i32, ctypes.POINTER(_UnitStep), i32,
                                          ctypes.POINTER(_Hparams), vp]),
         "fsdp_unflatten": (st, [vp, st, st, _c_void_p_p, _c_void_p_p, vp]),
+        "fsdp_reduce_shard_hybrid": (st, [vp, i32, _c_void_p_p, ctypes.c_double, vp, vp]),
+        "fsdp_reduce_adamw_shard_hybrid": (st, [vp, i32, _c_void_p_p, vp, vp, vp, vp,
+                                                ctypes.POINTER(_Hparams), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -259,6 +264,28 @@ def reduce_adamw_shard(unit: Unit, grads, master, exp_avg, exp_avg_sq, param_out
     c = hp._c(step, gs)
     _check(_lib.fsdp_reduce_adamw_shard(unit.handle, len(ptrs), _ptr_array(ptrs), p, m, v, w,
                                         ctypes.byref(c), _stream(stream, master.device)))
+
+
+def reduce_shard_hybrid(unit: Unit, replicas: int, grads, out: torch.Tensor,
+                        grad_scale: float | None = None, stream=None):
+    """Hybrid sharding: grads = replicas*F rows, replica-major."""
+    ptrs = _grad_ptrs(unit, grads)
+    gs = 1.0 / len(grads) if grad_scale is None else float(grad_scale)
+    o = _dev(out, torch.float32, "out", unit.shard_valid)
+    _check(_lib.fsdp_reduce_shard_hybrid(unit.handle, int(replicas), _ptr_array(ptrs), gs, o,
+                                         _stream(stream, out.device)))
+
+
+def reduce_adamw_shard_hybrid(unit: Unit, replicas: int, grads, master, exp_avg, exp_avg_sq,
+                              param_out, hp: AdamWHparams, step: int,
+                              grad_scale: float | None = None, stream=None):
+    ptrs = _grad_ptrs(unit, grads)
+    gs = 1.0 / len(grads) if grad_scale is None else float(grad_scale)
+    p, m, v, w = _state_ptrs(unit, master, exp_avg, exp_avg_sq, param_out)
+    c = hp._c(step, gs)
+    _check(_lib.fsdp_reduce_adamw_shard_hybrid(unit.handle, int(replicas), _ptr_array(ptrs),
+                                               p, m, v, w, ctypes.byref(c),
+                                               _stream(stream, master.device)))
 
 
 class UnitsStep:

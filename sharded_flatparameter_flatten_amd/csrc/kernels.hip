@@ -217,7 +217,7 @@ struct StepArgs {
   uint16_t* w;                        // bf16 parameter out, or null
   int64_t n;                          // shard_valid
   int32_t n_grads;
-  int32_t pad_;
+  int32_t group;                      // rows per replica group (== n_grads: one flat fold)
   Adam s;
 };
 
@@ -253,13 +253,56 @@ __device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, fl
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
 }
 
+// Hybrid sharding: rows [rho*group, (rho+1)*group) are one replica group. Each
+// group is left-folded on its own (the reduce-scatter inside the group), then
+// the group sums are left-folded in group order (the all-reduce across
+// groups), then scaled. Up to 8 rows of a group are loaded before they are
+// added.
+template <int SV>
+__device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, int ng, int group,
+                                                    float gs, int64_t i, float (&acc)[SV]) {
+  using G = typename BfVec<SV>::T;
+  for (int base = 0; base < ng; base += group) {
+    float part[SV];
+    unpack(ldh<G, kGradNt>(g[base] + i), part);
+    int k = 1;
+    for (; k + 8 <= group; k += 8) {
+      G q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(g[base + k + j] + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) accumulate(q[j], part);
+    }
+    for (; k < group; ++k) accumulate(ldh<G, kGradNt>(g[base + k] + i), part);
+    if (base == 0) {
+#pragma unroll
+      for (int e = 0; e < SV; ++e) acc[e] = part[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < SV; ++e) acc[e] = acc[e] + part[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
+}
+
+// Scalar form of the (flat or grouped) left fold of the rows at element i.
+__device__ __forceinline__ float reduce_element(const uint16_t* const* g, int ng, int group,
+                                                float gs, int64_t i) {
+  float acc = 0.f;
+  for (int base = 0; base < ng; base += group) {
+    float part = widen(g[base][i]);
+    for (int k = 1; k < group; ++k) part = part + widen(g[base + k][i]);
+    acc = base == 0 ? part : acc + part;
+  }
+  return acc * gs;
+}
+
 // One element of the fused step from raw pointers (tails of the vector paths).
 __device__ __forceinline__ void fused_scalar(const uint16_t* const* g, int ng, float* p_,
                                              float* m_, float* v_, uint16_t* w_, int64_t i,
                                              const Adam& s) {
-  float gr = widen(g[0][i]);
-  for (int k = 1; k < ng; ++k) gr = gr + widen(g[k][i]);
-  gr = gr * s.gs;
+  const float gr = reduce_element(g, ng, ng, s.gs, i);
   float p = p_[i], m = m_[i], v = v_[i];
   adamw(gr, p, m, v, s);
   p_[i] = p;
@@ -316,9 +359,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
   if constexpr (OP == Op::AdamW) {
     g = a.grad[i];
   } else {
-    g = widen(a.g[0][i]);
-    for (int k = 1; k < a.n_grads; ++k) g = g + widen(a.g[k][i]);
-    g = g * a.s.gs;
+    g = reduce_element(a.g, a.n_grads, a.group, a.s.gs, i);
   }
   if constexpr (OP == Op::Reduce) {
     a.out[i] = g;
@@ -347,7 +388,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
       if constexpr (OP == Op::AdamW) {
         loadf<kSV>(a.grad + i, g);
       } else {
-        reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+        if constexpr (NG == 0) {
+          if (a.group < a.n_grads) reduce_rows_grouped<kSV>(a.g, a.n_grads, a.group, a.s.gs, i, g);
+          else reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+        } else {
+          reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+        }
       }
       if constexpr (OP == Op::Reduce) {
         storef<kSV, kStepNt>(a.out + i, g);
@@ -632,6 +678,8 @@ template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
     k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);
+  } else if (a.group < a.n_grads) {
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);   // grouped fold
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
@@ -794,6 +842,7 @@ fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* 
         fsdp::range_of(w, u->valid, 2, false, who + "grads[" + std::to_string(k) + "]"));
   }
   a->n_grads = n_grads;
+  a->group = n_grads;
   return FSDP_OK;
 }
 
@@ -820,9 +869,9 @@ Path step_path(const StepArgs& a, Op op) {
   bool rows_ok = true;
   for (int k = 0; k < a.n_grads; ++k) rows_ok = rows_ok && aligned_bf16_vec(a.g[k]);
   if (rows_ok) return Path::Vector;
-  // the shifted path moves 4 elements per lane; its w store needs 8 bytes
-  if (kSV == 4 || !a.w || (reinterpret_cast<uintptr_t>(a.w) & 7u) == 0) return Path::Shifted;
-  return Path::Scalar;
+  // the shifted path folds the rows flat; grouped folds take the scalar path
+  if (a.group < a.n_grads) return Path::Scalar;
+  return Path::Shifted;
 }
 
 fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float* exp_avg_sq,
@@ -903,6 +952,53 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
   a.s = to_device(hs);
   return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
                                 "fsdp_reduce_adamw_shard");
+}
+
+fsdp_status fsdp_reduce_shard_hybrid(const fsdp_unit* u, int32_t replicas,
+                                     const void* const* grads, double grad_scale, float* out,
+                                     hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (replicas < 1 || int64_t(replicas) * u->F > FSDP_MAX_RANKS)
+    return fail(FSDP_ERR_INVALID_ARG, "replicas * F must be in [1, %d] (replicas=%d, F=%d)",
+                FSDP_MAX_RANKS, replicas, u->F);
+  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, replicas * u->F, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_f32(out, "out")) return st;
+  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.group = u->F;
+  a.out = out;
+  a.n = u->valid;
+  a.s.gs = static_cast<float>(grad_scale);
+  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream, "fsdp_reduce_shard_hybrid");
+}
+
+fsdp_status fsdp_reduce_adamw_shard_hybrid(const fsdp_unit* u, int32_t replicas,
+                                           const void* const* grads, float* master,
+                                           float* exp_avg, float* exp_avg_sq,
+                                           void* param_bf16_out, const fsdp_adamw_hparams* hp,
+                                           hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (replicas < 1 || int64_t(replicas) * u->F > FSDP_MAX_RANKS)
+    return fail(FSDP_ERR_INVALID_ARG, "replicas * F must be in [1, %d] (replicas=%d, F=%d)",
+                FSDP_MAX_RANKS, replicas, u->F);
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, replicas * u->F, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
+    return st;
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.group = u->F;
+  a.n = u->valid;
+  a.s = to_device(hs);
+  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
+                                "fsdp_reduce_adamw_shard_hybrid");
 }
 
 fsdp_status fsdp_reduce_adamw_units(int32_t n_units, const fsdp_unit_step* steps, int32_t n_grads,

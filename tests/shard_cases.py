@@ -23,13 +23,16 @@ HP = O.AdamW(**W.ADAMW)
 
 
 class Case:
-    """One rank's shard of one unit: shapes, F, rank, contributions, seeds."""
+    """One rank's shard of one unit: shapes, F, rank, contributions, seeds.
+
+    ``replicas`` > 1 is hybrid sharding: replicas*F rows, replica-major."""
 
     def __init__(self, shapes, F, rank, n_grads=None, config=0, outliers=False,
-                 grad_sigma=W.GRAD_SIGMA, master_sigma=W.MASTER_SIGMA):
+                 grad_sigma=W.GRAD_SIGMA, master_sigma=W.MASTER_SIGMA, replicas=1):
         self.shapes = [tuple(s) for s in shapes]
         self.F, self.rank = F, rank
-        self.n_grads = F if n_grads is None else n_grads
+        self.replicas = replicas
+        self.n_grads = F * replicas if n_grads is None else n_grads
         self.L = O.unit_layout(self.shapes, F, rank)
         self.config = config
         self.outliers = outliers
@@ -95,23 +98,32 @@ class Case:
         v = np.zeros_like(p)
         out = []
         for t in range(1, steps + 1):
-            res = O.reduce_adamw_shard(self.host_grads(t), L, p, m, v, HP, t,
-                                       grad_scale=1.0 / self.n_grads, emit_bf16=emit)
+            res = self._step(self.host_grads(t), L, p, m, v, t, emit)
             p, m, v = res[:3]
             out.append(res)
         return out
 
+    def _step(self, rows, L, p, m, v, t, emit):
+        if self.replicas > 1:
+            return O.reduce_adamw_shard_hybrid(rows, L, self.replicas, p, m, v, HP, t,
+                                               grad_scale=1.0 / self.n_grads, emit_bf16=emit)
+        return O.reduce_adamw_shard(rows, L, p, m, v, HP, t, grad_scale=1.0 / self.n_grads,
+                                    emit_bf16=emit)
+
     def oracle_sampled(self, loc, steps, emit=True):
         """Oracle trajectory at local shard indices ``loc`` only."""
         g = self.L.shard_begin + np.asarray(loc, dtype=np.int64)
-        one = O.unit_layout([(g.size,)], 1, 0)
+        # a layout of the sampled elements only: F kept (the hybrid groups rows by F),
+        # rank 0 of a unit whose shard is exactly the sample
+        one = O.unit_layout([(g.size * self.F,)], self.F, 0)
         p = self.host_master_at(g)
         m = np.zeros_like(p)
         v = np.zeros_like(p)
         out = []
         for t in range(1, steps + 1):
-            res = O.reduce_adamw_shard(self.host_grads_at(t, g), one, p, m, v, HP, t,
-                                       grad_scale=1.0 / self.n_grads, emit_bf16=emit)
+            rows = [np.concatenate([r, np.zeros(g.size * (self.F - 1), np.uint16)])
+                    for r in self.host_grads_at(t, g)]
+            res = self._step(rows, one, p, m, v, t, emit)
             p, m, v = res[:3]
             out.append(res)
         return out

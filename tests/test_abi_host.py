@@ -194,3 +194,17 @@ def test_multi_unit_step_validates_across_units(lib):
     assert raw.fsdp_reduce_adamw_units(-1, None, 8, hp, None) == 1
     arr = (lib._UnitStep * 1)(step(rows0, 0))
     assert raw.fsdp_reduce_adamw_units(1, arr, 0, hp, None) == 1
+
+
+def test_hybrid_entry_points_validate_before_launch(lib):
+    raw = _raw(lib)
+    u = lib.Unit([(4096,)], 8, 2)
+    rows = lib._ptr_array([FAKE + k * (1 << 20) for k in range(64)])
+    p, m, v = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    hp = ctypes.byref(_hp(lib))
+    assert raw.fsdp_reduce_adamw_shard_hybrid(u.handle, 9, rows, p, m, v, None, hp, None) == 1
+    assert "replicas * F" in raw.fsdp_last_error().decode()
+    assert raw.fsdp_reduce_adamw_shard_hybrid(u.handle, 0, rows, p, m, v, None, hp, None) == 1
+    assert raw.fsdp_reduce_shard_hybrid(u.handle, 2, rows, float("nan"), p, None) == 1
+    win = FAKE + 5 * (1 << 20) + 2 * u.shard_begin
+    assert raw.fsdp_reduce_shard_hybrid(u.handle, 2, rows, 0.0625, win, None) == 3

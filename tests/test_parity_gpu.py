@@ -426,3 +426,55 @@ def test_shifted_rows_with_aligned_state(shift, ng, fused):
     want = case.oracle_full(1)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
         assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"{name} bits")
+
+
+# ---------------------------------------------------------------------------
+# hybrid sharding (HSDP): R replica groups of F ranks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,F", [(2, 2), (2, 4), (3, 4), (2, 8), (4, 8)])
+def test_hybrid_fused_every_rank_every_element(R, F):
+    shapes = [(1000, 7), (33,)]
+    for rank in range(F):
+        case = Case(shapes, F, rank, config=30, replicas=R)
+        u = fsdp.Unit(shapes, F, rank)
+        grads = case.device_grads(1)
+        flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], F)
+        p = torch.from_numpy(flat.view(np.float32)[u.shard_begin:u.shard_begin + u.S].copy()).to(DEV)
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+        fsdp.reduce_adamw_shard_hybrid(u, R, grads, p, m, v, w, HPD, 1)
+        torch.cuda.synchronize()
+        want = case.oracle_full(1)[-1]
+        n = u.shard_valid
+        for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+            assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"R={R} F={F} r={rank} {name}")
+
+
+@pytest.mark.parametrize("R,F,rank", [(2, 4, 1), (3, 7, 3)])      # F=7: odd S, scalar path
+def test_hybrid_reduce_shard_every_element(R, F, rank):
+    shapes = [(2049,), (7, 9)]
+    case = Case(shapes, F, rank, config=31, replicas=R)
+    u = fsdp.Unit(shapes, F, rank)
+    grads = case.device_grads(1)
+    out = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.reduce_shard_hybrid(u, R, grads, out)
+    torch.cuda.synchronize()
+    want = O.reduce_shard_hybrid(case.host_grads(1), case.L, R)
+    assert_bits(to_np(out)[:u.shard_valid].view(np.uint32), want.view(np.uint32), "hybrid reduce")
+
+
+def test_hybrid_blk7_two_groups_of_8_sampled():
+    case = Case(W.shapes(W.BLK7), 8, 5, config=32, replicas=2)
+    u = fsdp.Unit(case.shapes, 8, 5)
+    grads = case.device_grads(1)
+    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.flatten_pad(u, case.device_master_tensors(), p)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    fsdp.reduce_adamw_shard_hybrid(u, 2, grads, p, m, v, w, HPD, 1)
+    torch.cuda.synchronize()
+    loc = case.sample_indices()
+    want = case.oracle_sampled(loc, 1)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(gather(got, loc)), _bits(exp), f"hybrid blk7 {name}")
