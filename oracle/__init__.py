@@ -12,8 +12,10 @@ from .fsdp_oracle import (  # noqa: F401
     numel,
     persistent_bytes,
     reduce_adamw_shard,
+    reduce_adamw_shard_bf16acc,
     reduce_adamw_shard_hybrid,
     reduce_shard,
+    reduce_shard_bf16acc,
     reduce_shard_hybrid,
     unflatten,
     unit_layout,

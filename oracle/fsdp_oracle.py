@@ -28,7 +28,7 @@ the learning rate (decay applied as lr * wd * p).
 Parity status of each function (see the pins in tests/test_oracle_pins.py):
 ``unit_layout``, ``flatten_pad``, ``reduce_shard``, ``adamw_step``,
 ``bf16_round_nearest_even``, ``unflatten`` (bf16 and fp32 outputs), ``cast_unflatten``,
-``reduce_shard_hybrid``, ``persistent_bytes`` are
+``reduce_shard_hybrid``, ``reduce_shard_bf16acc``, ``persistent_bytes`` are
 pinned. Parity unpinned: the choice of one binary32 op order among the
 mathematically equal ones (fixed by this file), and NaN payloads other than the
 canonical quiet NaN.
@@ -197,6 +197,41 @@ def reduce_shard(grads, layout: UnitLayout, grad_scale: float | None = None) -> 
     for k in range(1, n):
         acc = acc + bf16_widen(grads[k][lo:hi])
     return acc * gs
+
+
+def reduce_shard_bf16acc(grads, layout: UnitLayout, grad_scale: float | None = None) -> np.ndarray:
+    """The reduce-scatter arithmetic with bf16 partial sums (reduce dtype bf16).
+
+    [NOTE-003, "Recommendations"] (R3): mixed precision for communication
+    volume as much as for memory; [Glossary, "FSDP Implementation (PyTorch)"
+    -> Mixed Precision]: the reduce dtype is a choice (fp32 there). Reading of
+    a reduce-scatter that keeps its partials in bf16: a left fold in rank
+    order where every addition is one binary32 addition of the two bf16
+    values followed by rounding the partial to bf16 (nearest even); the final
+    bf16 sum is widened and multiplied by fp32(grad_scale). Numerics pinned by
+    closed forms and the summation bound with bf16's unit roundoff, not by
+    parity with the fp32 reduction.
+    """
+    n = len(grads)
+    if n < 1:
+        raise ValueError("need at least one gradient buffer")
+    if grad_scale is None:
+        grad_scale = 1.0 / n
+    gs = np.float32(grad_scale)
+    lo = layout.shard_begin
+    hi = lo + layout.shard_valid
+    partial = np.asarray(grads[0][lo:hi], dtype=np.uint16)
+    for k in range(1, n):
+        total = bf16_widen(partial) + bf16_widen(grads[k][lo:hi])
+        partial = bf16_round_nearest_even(total)
+    return bf16_widen(partial) * gs
+
+
+def reduce_adamw_shard_bf16acc(grads, layout: UnitLayout, p, m, v, hp, step: int,
+                               grad_scale: float | None = None, emit_bf16: bool = False):
+    """The bf16-partials reduction followed by ``adamw_step`` on its fp32 result."""
+    g = reduce_shard_bf16acc(grads, layout, grad_scale)
+    return adamw_step(g, p, m, v, hp, step, emit_bf16)
 
 
 def reduce_shard_hybrid(grads, layout: UnitLayout, replicas: int,

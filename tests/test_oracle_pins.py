@@ -331,6 +331,35 @@ def test_reduce_brute_force_fractions_tiny():
             assert abs(Fraction(float(got[e])) - exact) <= gamma * mag
 
 
+def test_bf16acc_reduce_closed_forms():
+    n = 1 << 14
+    a, b = rng_bf16(121, n, 1e-3, 0), rng_bf16(121, n, 1e-3, 1)
+    L = O.unit_layout([(n,)], 1, 0)
+    # one row: the bf16 value itself, times the scale
+    assert np.array_equal(O.reduce_shard_bf16acc([a], L), O.bf16_widen(a))
+    # two rows: torch's bf16 rounding of the fp32 sum (itself one rounding of the exact sum)
+    got = O.reduce_shard_bf16acc([a, b], L, grad_scale=1.0)
+    s32 = (O.bf16_widen(a).astype(np.float64) + O.bf16_widen(b).astype(np.float64)).astype(np.float32)
+    ref = torch.from_numpy(s32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_bf16acc_reduce_within_bf16_summation_bound():
+    n_el, n = 1 << 14, 8
+    gs = [datagen.bf16_bits_host(datagen.seed_for(3, 1), k, np.arange(n_el), 1e-3,
+                                 outlier_seed=datagen.seed_for(3, 2)) for k in range(n)]
+    L = O.unit_layout([(n_el,)], 1, 0)
+    got = O.reduce_shard_bf16acc(gs, L, grad_scale=1.0).astype(np.float64)
+    vals = np.stack([O.bf16_widen(g).astype(np.float64) for g in gs])
+    u = 2.0 ** -8 + U32 + 2.0 ** -8 * U32       # fp32 add then bf16 rounding, per step
+    gamma = (n - 1) * u / (1 - (n - 1) * u)
+    err = np.abs(got - vals.sum(axis=0))
+    assert np.all(err <= gamma * np.abs(vals).sum(axis=0))
+    # and it really is coarser than the fp32 reduction on these inputs
+    fp32 = O.reduce_shard(gs, L, grad_scale=1.0).astype(np.float64)
+    assert np.abs(fp32 - vals.sum(axis=0)).max() < err.max()
+
+
 def test_hybrid_reduce_special_cases_reduce_to_the_flat_fold():
     shapes = [(777,)]
     rows8 = [rng_bf16(101, 777, 1e-3, k) for k in range(8)]
