@@ -308,6 +308,8 @@ def hybrid_bench(args):
     for name, fn in (("hybrid", lambda i: fsdp.reduce_adamw_shard_hybrid(
                           u, Rg, rows[i % R], *state[i % R], hp, 2, stream=stream)),
                      ("flat_16_rows", lambda i: fsdp.reduce_adamw_shard(
+                          u, rows[i % R], *state[i % R], hp, 2, stream=stream)),
+                     ("flat_16_rows_bf16_partials", lambda i: fsdp.reduce_adamw_shard_bf16acc(
                           u, rows[i % R], *state[i % R], hp, 2, stream=stream))):
         for i in range(max(args.warmup, R)):
             fn(i)
@@ -322,7 +324,7 @@ def hybrid_bench(args):
         nbytes = (2 * Rg * F + 26) * u.shard_valid
         res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
                      "frac_of_8TBps": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
-    print(json.dumps({"metric": "hybrid-sharding fused shard step (2 groups x F=8)",
+    print(json.dumps({"metric": "hybrid-sharding and bf16-partials fused shard step (16 rows)",
                       "workload": "7B block unit, F=8, 2 replica groups, rank 0",
                       "rotating_sets": R, **res}), flush=True)
 

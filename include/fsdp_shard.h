@@ -172,6 +172,23 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* unit, int32_t n_grads,
                                     void* param_bf16_out,
                                     const fsdp_adamw_hparams* hp, hipStream_t stream);
 
+/* Reduce dtype bf16: the reduce-scatter arithmetic with bf16 partial sums.
+ * [NOTE-003, "Recommendations"] (R3): mixed precision for communication volume;
+ * [Glossary, "FSDP Implementation (PyTorch)" -> Mixed Precision]: the reduce
+ * dtype is a choice. For i < shard_valid: p = grads[0][r*S+i]; for k = 1..n-1:
+ * p = bf16_rne(widen(p) + widen(grads[k][r*S+i])) (an fp32 add, then rounding
+ * to nearest even bf16); out[i] = widen(p) * fp32(grad_scale). Same buffers and
+ * rules as fsdp_reduce_shard / fsdp_reduce_adamw_shard; only the numerics of
+ * the sum differ (coarser, bounded by the summation bound in bf16). */
+fsdp_status fsdp_reduce_shard_bf16acc(const fsdp_unit* unit, int32_t n_grads,
+                                      const void* const* grads, double grad_scale, float* out,
+                                      hipStream_t stream);
+fsdp_status fsdp_reduce_adamw_shard_bf16acc(const fsdp_unit* unit, int32_t n_grads,
+                                            const void* const* grads, float* master,
+                                            float* exp_avg, float* exp_avg_sq,
+                                            void* param_bf16_out,
+                                            const fsdp_adamw_hparams* hp, hipStream_t stream);
+
 /* Hybrid sharding (HSDP): the unit is sharded F ways inside each of `replicas`
  * (R) groups and replicated across groups. [NOTE-003, "Concepts"]: shard within
  * a group, replicate across groups; [Glossary, "Hybrid Sharding"]: gradients

@@ -16,6 +16,7 @@ Names follow the C ABI in include/fsdp_shard.h:
                                             -> fsdp_reduce_adamw_shard
 * ``reduce_adamw_units(steps, hp, step)``   -> fsdp_reduce_adamw_units
 * ``reduce_shard_hybrid`` / ``reduce_adamw_shard_hybrid`` -> the hybrid-sharding forms
+* ``reduce_shard_bf16acc`` / ``reduce_adamw_shard_bf16acc`` -> bf16 partial sums
 * ``cast_unflatten(unit, shards, outs)``    -> fsdp_cast_unflatten (bf16 outputs)
 * ``unflatten(unit, shards, outs)``         -> fsdp_unflatten (dtypes from the tensors)
 """
@@ -31,7 +32,8 @@ import torch
 __all__ = [
     "FsdpError", "Unit", "AdamWHparams", "flatten_pad", "reduce_shard", "adamw_shard",
     "reduce_adamw_shard", "reduce_adamw_units", "UnitsStep", "cast_unflatten", "unflatten",
-    "reduce_shard_hybrid", "reduce_adamw_shard_hybrid", "abi_version", "library_path",
+    "reduce_shard_hybrid", "reduce_adamw_shard_hybrid", "reduce_shard_bf16acc",
+    "reduce_adamw_shard_bf16acc", "abi_version", "library_path",
     "F32", "BF16",
 ]
 
@@ -104,6 +106,9 @@ def _load():
                                          ctypes.POINTER(_Hparams), vp]),
         "fsdp_unflatten": (st, [vp, st, st, _c_void_p_p, _c_void_p_p, vp]),
         "fsdp_reduce_shard_hybrid": (st, [vp, i32, _c_void_p_p, ctypes.c_double, vp, vp]),
+        "fsdp_reduce_shard_bf16acc": (st, [vp, i32, _c_void_p_p, ctypes.c_double, vp, vp]),
+        "fsdp_reduce_adamw_shard_bf16acc": (st, [vp, i32, _c_void_p_p, vp, vp, vp, vp,
+                                                 ctypes.POINTER(_Hparams), vp]),
         "fsdp_reduce_adamw_shard_hybrid": (st, [vp, i32, _c_void_p_p, vp, vp, vp, vp,
                                                 ctypes.POINTER(_Hparams), vp]),
     }
@@ -264,6 +269,29 @@ def reduce_adamw_shard(unit: Unit, grads, master, exp_avg, exp_avg_sq, param_out
     c = hp._c(step, gs)
     _check(_lib.fsdp_reduce_adamw_shard(unit.handle, len(ptrs), _ptr_array(ptrs), p, m, v, w,
                                         ctypes.byref(c), _stream(stream, master.device)))
+
+
+def reduce_shard_bf16acc(unit: Unit, grads, out: torch.Tensor, grad_scale: float | None = None,
+                         stream=None):
+    """reduce_shard with bf16 partial sums (reduce dtype bf16)."""
+    ptrs = _grad_ptrs(unit, grads)
+    gs = 1.0 / len(grads) if grad_scale is None else float(grad_scale)
+    o = _dev(out, torch.float32, "out", unit.shard_valid)
+    _check(_lib.fsdp_reduce_shard_bf16acc(unit.handle, len(ptrs), _ptr_array(ptrs), gs, o,
+                                          _stream(stream, out.device)))
+
+
+def reduce_adamw_shard_bf16acc(unit: Unit, grads, master, exp_avg, exp_avg_sq, param_out,
+                               hp: AdamWHparams, step: int, grad_scale: float | None = None,
+                               stream=None):
+    """reduce_adamw_shard with bf16 partial sums (reduce dtype bf16)."""
+    ptrs = _grad_ptrs(unit, grads)
+    gs = 1.0 / len(grads) if grad_scale is None else float(grad_scale)
+    p, m, v, w = _state_ptrs(unit, master, exp_avg, exp_avg_sq, param_out)
+    c = hp._c(step, gs)
+    _check(_lib.fsdp_reduce_adamw_shard_bf16acc(unit.handle, len(ptrs), _ptr_array(ptrs),
+                                                p, m, v, w, ctypes.byref(c),
+                                                _stream(stream, master.device)))
 
 
 def reduce_shard_hybrid(unit: Unit, replicas: int, grads, out: torch.Tensor,

@@ -218,6 +218,8 @@ struct StepArgs {
   int64_t n;                          // shard_valid
   int32_t n_grads;
   int32_t group;                      // rows per replica group (== n_grads: one flat fold)
+  int32_t bf16acc;                    // 1: every partial sum rounded to bf16
+  int32_t pad_;
   Adam s;
 };
 
@@ -253,13 +255,33 @@ __device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, fl
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
 }
 
-// Hybrid sharding: rows [rho*group, (rho+1)*group) are one replica group. Each
-// group is left-folded on its own (the reduce-scatter inside the group), then
-// the group sums are left-folded in group order (the all-reduce across
-// groups), then scaled. Up to 8 rows of a group are loaded before they are
-// added.
-template <int SV>
-__device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, int ng, int group,
+// fp32 value -> nearest bf16 (ties to even), kept as an fp32 value.
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(to_bf16(f) << 16); }
+
+// x += row, with every partial rounded to bf16 when BACC.
+template <bool BACC>
+__device__ __forceinline__ void add_row(u32x2 q, float (&x)[4]) {
+  float t[4];
+  unpack(q, t);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = BACC ? round_bf16(x[e] + t[e]) : x[e] + t[e];
+}
+template <bool BACC>
+[[maybe_unused]] __device__ __forceinline__ void add_row(u32x4 q, float (&x)[8]) {
+  float t[8];
+  unpack(q, t);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = BACC ? round_bf16(x[e] + t[e]) : x[e] + t[e];
+}
+
+// The general left fold, for hybrid sharding and for bf16 partial sums. Rows
+// [rho*group, (rho+1)*group) are one replica group: each group is folded on
+// its own (the reduce-scatter inside the group), then the group sums are
+// folded in group order (the all-reduce across groups), then scaled. With
+// BACC every addition is an fp32 add followed by rounding to bf16. Up to 8
+// rows of a group are loaded before they are added.
+template <int SV, bool BACC>
+__device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, int ng, int group,
                                                     float gs, int64_t i, float (&acc)[SV]) {
   using G = typename BfVec<SV>::T;
   for (int base = 0; base < ng; base += group) {
@@ -271,29 +293,37 @@ __device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, in
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(g[base + k + j] + i);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) accumulate(q[j], part);
+      for (int j = 0; j < 8; ++j) add_row<BACC>(q[j], part);
     }
-    for (; k < group; ++k) accumulate(ldh<G, kGradNt>(g[base + k] + i), part);
+    for (; k < group; ++k) add_row<BACC>(ldh<G, kGradNt>(g[base + k] + i), part);
     if (base == 0) {
 #pragma unroll
       for (int e = 0; e < SV; ++e) acc[e] = part[e];
     } else {
 #pragma unroll
-      for (int e = 0; e < SV; ++e) acc[e] = acc[e] + part[e];
+      for (int e = 0; e < SV; ++e) acc[e] = BACC ? round_bf16(acc[e] + part[e]) : acc[e] + part[e];
     }
   }
 #pragma unroll
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
 }
 
-// Scalar form of the (flat or grouped) left fold of the rows at element i.
+// Scalar form of the general fold of the rows at element i.
 __device__ __forceinline__ float reduce_element(const uint16_t* const* g, int ng, int group,
-                                                float gs, int64_t i) {
+                                                bool bacc, float gs, int64_t i) {
   float acc = 0.f;
   for (int base = 0; base < ng; base += group) {
     float part = widen(g[base][i]);
-    for (int k = 1; k < group; ++k) part = part + widen(g[base + k][i]);
-    acc = base == 0 ? part : acc + part;
+    for (int k = 1; k < group; ++k) {
+      part = part + widen(g[base + k][i]);
+      if (bacc) part = round_bf16(part);
+    }
+    if (base == 0) {
+      acc = part;
+    } else {
+      acc = acc + part;
+      if (bacc) acc = round_bf16(acc);
+    }
   }
   return acc * gs;
 }
@@ -302,7 +332,7 @@ __device__ __forceinline__ float reduce_element(const uint16_t* const* g, int ng
 __device__ __forceinline__ void fused_scalar(const uint16_t* const* g, int ng, float* p_,
                                              float* m_, float* v_, uint16_t* w_, int64_t i,
                                              const Adam& s) {
-  const float gr = reduce_element(g, ng, ng, s.gs, i);
+  const float gr = reduce_element(g, ng, ng, false, s.gs, i);
   float p = p_[i], m = m_[i], v = v_[i];
   adamw(gr, p, m, v, s);
   p_[i] = p;
@@ -359,7 +389,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
   if constexpr (OP == Op::AdamW) {
     g = a.grad[i];
   } else {
-    g = reduce_element(a.g, a.n_grads, a.group, a.s.gs, i);
+    g = reduce_element(a.g, a.n_grads, a.group, a.bf16acc != 0, a.s.gs, i);
   }
   if constexpr (OP == Op::Reduce) {
     a.out[i] = g;
@@ -389,8 +419,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
         loadf<kSV>(a.grad + i, g);
       } else {
         if constexpr (NG == 0) {
-          if (a.group < a.n_grads) reduce_rows_grouped<kSV>(a.g, a.n_grads, a.group, a.s.gs, i, g);
-          else reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+          if (a.bf16acc)
+            reduce_rows_general<kSV, true>(a.g, a.n_grads, a.group, a.s.gs, i, g);
+          else if (a.group < a.n_grads)
+            reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, i, g);
+          else
+            reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, i, g);
         } else {
           reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
         }
@@ -678,8 +712,8 @@ template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
     k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);
-  } else if (a.group < a.n_grads) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);   // grouped fold
+  } else if (a.group < a.n_grads || a.bf16acc) {
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);   // general fold
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
@@ -869,8 +903,8 @@ Path step_path(const StepArgs& a, Op op) {
   bool rows_ok = true;
   for (int k = 0; k < a.n_grads; ++k) rows_ok = rows_ok && aligned_bf16_vec(a.g[k]);
   if (rows_ok) return Path::Vector;
-  // the shifted path folds the rows flat; grouped folds take the scalar path
-  if (a.group < a.n_grads) return Path::Scalar;
+  // the shifted path folds the rows flat in fp32; other folds take the scalar path
+  if (a.group < a.n_grads || a.bf16acc) return Path::Scalar;
   return Path::Shifted;
 }
 
@@ -952,6 +986,48 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
   a.s = to_device(hs);
   return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
                                 "fsdp_reduce_adamw_shard");
+}
+
+fsdp_status fsdp_reduce_shard_bf16acc(const fsdp_unit* u, int32_t n_grads,
+                                      const void* const* grads, double grad_scale, float* out,
+                                      hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_f32(out, "out")) return st;
+  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.bf16acc = 1;
+  a.out = out;
+  a.n = u->valid;
+  a.s.gs = static_cast<float>(grad_scale);
+  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream,
+                                 "fsdp_reduce_shard_bf16acc");
+}
+
+fsdp_status fsdp_reduce_adamw_shard_bf16acc(const fsdp_unit* u, int32_t n_grads,
+                                            const void* const* grads, float* master,
+                                            float* exp_avg, float* exp_avg_sq,
+                                            void* param_bf16_out, const fsdp_adamw_hparams* hp,
+                                            hipStream_t stream) {
+  fsdp::clear_error();
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
+  StepArgs a{};
+  std::vector<fsdp::ByteRange> ranges;
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
+    return st;
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.bf16acc = 1;
+  a.n = u->valid;
+  a.s = to_device(hs);
+  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
+                                "fsdp_reduce_adamw_shard_bf16acc");
 }
 
 fsdp_status fsdp_reduce_shard_hybrid(const fsdp_unit* u, int32_t replicas,

@@ -28,10 +28,12 @@ class Case:
     ``replicas`` > 1 is hybrid sharding: replicas*F rows, replica-major."""
 
     def __init__(self, shapes, F, rank, n_grads=None, config=0, outliers=False,
-                 grad_sigma=W.GRAD_SIGMA, master_sigma=W.MASTER_SIGMA, replicas=1):
+                 grad_sigma=W.GRAD_SIGMA, master_sigma=W.MASTER_SIGMA, replicas=1,
+                 bf16acc=False):
         self.shapes = [tuple(s) for s in shapes]
         self.F, self.rank = F, rank
         self.replicas = replicas
+        self.bf16acc = bf16acc
         self.n_grads = F * replicas if n_grads is None else n_grads
         self.L = O.unit_layout(self.shapes, F, rank)
         self.config = config
@@ -104,6 +106,9 @@ class Case:
         return out
 
     def _step(self, rows, L, p, m, v, t, emit):
+        if self.bf16acc:
+            return O.reduce_adamw_shard_bf16acc(rows, L, p, m, v, HP, t,
+                                                grad_scale=1.0 / self.n_grads, emit_bf16=emit)
         if self.replicas > 1:
             return O.reduce_adamw_shard_hybrid(rows, L, self.replicas, p, m, v, HP, t,
                                                grad_scale=1.0 / self.n_grads, emit_bf16=emit)

@@ -478,3 +478,56 @@ def test_hybrid_blk7_two_groups_of_8_sampled():
     want = case.oracle_sampled(loc, 1)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
         assert_bits(_bits(gather(got, loc)), _bits(exp), f"hybrid blk7 {name}")
+
+
+# ---------------------------------------------------------------------------
+# reduce dtype bf16: bf16 partial sums
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shapes,F,ng", [([(1000, 7), (33,)], 4, 4), ([(1000, 7), (33,)], 8, 8),
+                                         ([(5000,)], 4, 12), ([(1000, 3), (17,)], 7, 7)])
+def test_bf16acc_fused_every_rank_every_element(shapes, F, ng):
+    for rank in range(F):
+        case = Case(shapes, F, rank, n_grads=ng, config=40, outliers=True, bf16acc=True)
+        u = fsdp.Unit(shapes, F, rank)
+        grads = case.device_grads(1)
+        flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], F)
+        p = torch.from_numpy(flat.view(np.float32)[u.shard_begin:u.shard_begin + u.S].copy()).to(DEV)
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+        fsdp.reduce_adamw_shard_bf16acc(u, grads, p, m, v, w, HPD, 1)
+        torch.cuda.synchronize()
+        want = case.oracle_full(1)[-1]
+        n = u.shard_valid
+        for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+            assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"bf16acc F={F} r={rank} {name}")
+
+
+def test_bf16acc_reduce_shard_every_element_and_coarser_than_fp32():
+    shapes, F, rank = [(4096, 5)], 4, 2
+    case = Case(shapes, F, rank, config=41, outliers=True, bf16acc=True)
+    u = fsdp.Unit(shapes, F, rank)
+    grads = case.device_grads(1)
+    out = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.reduce_shard_bf16acc(u, grads, out)
+    torch.cuda.synchronize()
+    host = case.host_grads(1)
+    want = O.reduce_shard_bf16acc(host, case.L)
+    assert_bits(to_np(out).view(np.uint32), want.view(np.uint32), "bf16acc reduce")
+    assert not np.array_equal(want, O.reduce_shard(host, case.L))
+
+
+def test_bf16acc_blk7_sampled():
+    case = Case(W.shapes(W.BLK7), 8, 3, config=42, outliers=True, bf16acc=True)
+    u = fsdp.Unit(case.shapes, 8, 3)
+    grads = case.device_grads(1)
+    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.flatten_pad(u, case.device_master_tensors(), p)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    fsdp.reduce_adamw_shard_bf16acc(u, grads, p, m, v, w, HPD, 1)
+    torch.cuda.synchronize()
+    loc = case.sample_indices()
+    want = case.oracle_sampled(loc, 1)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(gather(got, loc)), _bits(exp), f"bf16acc blk7 {name}")
