@@ -48,9 +48,6 @@
 #ifndef FSDP_STEP_BLOCK
 #define FSDP_STEP_BLOCK 256   // threads per workgroup, reduce/AdamW kernels
 #endif
-#ifndef FSDP_STEP_VEC
-#define FSDP_STEP_VEC 4       // consecutive elements per lane in the step kernels (4 or 8)
-#endif
 #ifndef FSDP_GRAD_NT_LOAD
 #define FSDP_GRAD_NT_LOAD 1   // streaming hint on the gradient-row loads (read once)
 #endif
@@ -73,9 +70,8 @@ namespace {
 
 constexpr int kThreads = FSDP_COPY_BLOCK;
 constexpr int kStepThreads = FSDP_STEP_BLOCK;
-constexpr int kSV = FSDP_STEP_VEC;
+constexpr int kSV = 4;   // consecutive elements per lane in the step kernels
 constexpr int64_t kStepTile = int64_t(kStepThreads) * kSV;
-static_assert(kSV == 4 || kSV == 8, "step kernels move 4 or 8 elements per lane");
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -140,47 +136,15 @@ constexpr bool kGradNt = FSDP_GRAD_NT_LOAD != 0;
 constexpr bool kCopyNtLoad = FSDP_COPY_NT_LOAD != 0;
 constexpr bool kStateNt = FSDP_STATE_NT_LOAD != 0;
 
-__device__ __forceinline__ void unpack8(u32x4 q, float (&x)[8]) {
-  x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
-  x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
-  x[4] = lo_bf16(q.z); x[5] = hi_bf16(q.z);
-  x[6] = lo_bf16(q.w); x[7] = hi_bf16(q.w);
-}
-
-__device__ __forceinline__ void accumulate8(u32x4 q, float (&x)[8]) {
-  x[0] = x[0] + lo_bf16(q.x); x[1] = x[1] + hi_bf16(q.x);
-  x[2] = x[2] + lo_bf16(q.y); x[3] = x[3] + hi_bf16(q.y);
-  x[4] = x[4] + lo_bf16(q.z); x[5] = x[5] + hi_bf16(q.z);
-  x[6] = x[6] + lo_bf16(q.w); x[7] = x[7] + hi_bf16(q.w);
-}
-
-template <bool NT>
-__device__ __forceinline__ void store8_bf16(uint16_t* p, const float (&x)[8]) {
-  st<u32x4, NT>(p, u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
-                         pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])});
-}
-
-// Width-generic forms for the step kernels: a lane's SV consecutive elements
-// are one 8-byte (SV = 4) or 16-byte (SV = 8) bf16 access and SV/4 16-byte
-// fp32 accesses.
-template <int SV>
-struct BfVec;
-template <>
-struct BfVec<4> { using T = u32x2; };
-template <>
-struct BfVec<8> { using T = u32x4; };
-
-[[maybe_unused]] __device__ __forceinline__ void unpack(u32x2 q, float (&x)[4]) {
+// A lane's 4 consecutive elements: one 8-byte bf16 access per row and one
+// 16-byte access per fp32 array.
+__device__ __forceinline__ void unpack(u32x2 q, float (&x)[4]) {
   x[0] = lo_bf16(q.x); x[1] = hi_bf16(q.x);
   x[2] = lo_bf16(q.y); x[3] = hi_bf16(q.y);
 }
-[[maybe_unused]] __device__ __forceinline__ void unpack(u32x4 q, float (&x)[8]) { unpack8(q, x); }
-[[maybe_unused]] __device__ __forceinline__ void accumulate(u32x2 q, float (&x)[4]) {
+__device__ __forceinline__ void accumulate(u32x2 q, float (&x)[4]) {
   x[0] = x[0] + lo_bf16(q.x); x[1] = x[1] + hi_bf16(q.x);
   x[2] = x[2] + lo_bf16(q.y); x[3] = x[3] + hi_bf16(q.y);
-}
-[[maybe_unused]] __device__ __forceinline__ void accumulate(u32x4 q, float (&x)[8]) {
-  accumulate8(q, x);
 }
 
 template <int SV>
@@ -199,8 +163,8 @@ __device__ __forceinline__ void storef(float* p, const float (&x)[SV]) {
 }
 template <int SV, bool NT>
 __device__ __forceinline__ void store_bf16(uint16_t* p, const float (&x)[SV]) {
-  if constexpr (SV == 4) st<u32x2, NT>(p, u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
-  else store8_bf16<NT>(p, x);
+  static_assert(SV == 4, "4 elements per lane");
+  st<u32x2, NT>(p, u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
 }
 
 // ---------------------------------------------------------------------------
@@ -231,7 +195,7 @@ enum class Op { Reduce, AdamW, Fused };
 template <int NG, int SV>
 __device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, float gs,
                                             int64_t i, float (&acc)[SV]) {
-  using G = typename BfVec<SV>::T;
+  using G = u32x2;
   if constexpr (NG > 0) {
     G q[NG];
 #pragma unroll
@@ -266,13 +230,6 @@ __device__ __forceinline__ void add_row(u32x2 q, float (&x)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) x[e] = BACC ? round_bf16(x[e] + t[e]) : x[e] + t[e];
 }
-template <bool BACC>
-[[maybe_unused]] __device__ __forceinline__ void add_row(u32x4 q, float (&x)[8]) {
-  float t[8];
-  unpack(q, t);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = BACC ? round_bf16(x[e] + t[e]) : x[e] + t[e];
-}
 
 // The general left fold, for hybrid sharding and for bf16 partial sums. Rows
 // [rho*group, (rho+1)*group) are one replica group: each group is folded on
@@ -283,7 +240,7 @@ template <bool BACC>
 template <int SV, bool BACC>
 __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, int ng, int group,
                                                     float gs, int64_t i, float (&acc)[SV]) {
-  using G = typename BfVec<SV>::T;
+  using G = u32x2;
   for (int base = 0; base < ng; base += group) {
     float part[SV];
     unpack(ldh<G, kGradNt>(g[base] + i), part);
@@ -694,10 +651,8 @@ __global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
 // ---------------------------------------------------------------------------
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-// a lane's kSV bf16 elements form one 2*kSV-byte access
-bool aligned_bf16_vec(const void* p) {
-  return (reinterpret_cast<uintptr_t>(p) & uintptr_t(2 * kSV - 1)) == 0;
-}
+// a lane's 4 bf16 elements form one 8-byte access
+bool aligned_bf16_vec(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 unsigned grid_for(int64_t tiles) { return static_cast<unsigned>(std::max<int64_t>(tiles, 1)); }
 

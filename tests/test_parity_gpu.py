@@ -531,3 +531,31 @@ def test_bf16acc_blk7_sampled():
     want = case.oracle_sampled(loc, 1)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
         assert_bits(_bits(gather(got, loc)), _bits(exp), f"bf16acc blk7 {name}")
+
+
+def test_sharded_steps_concatenated_equal_the_ddp_step():
+    """[NOTE-003, "Key results"]: F = 1 is plain data parallelism. All 8 ranks' F=8 shard
+    steps, concatenated, equal the F=1 step over the same 8 gradient rows, bitwise."""
+    shapes = W.shapes(W.BLK7)
+    rows = Case(shapes, 8, 0, config=43).device_grads(1)
+    ddp = fsdp.Unit(shapes, 1, 0)
+    masters = Case(shapes, 8, 0, config=43).device_master_tensors()
+    full = [torch.empty(ddp.S, dtype=torch.float32, device=DEV)]
+    fsdp.flatten_pad(ddp, masters, full[0])
+    full += [torch.zeros_like(full[0]), torch.zeros_like(full[0]),
+             torch.empty(ddp.S, dtype=torch.bfloat16, device=DEV)]
+    shards = []
+    for r in range(8):
+        u = fsdp.Unit(shapes, 8, r)
+        st = [full[0][u.shard_begin:u.shard_begin + u.S].clone()]
+        st += [torch.zeros_like(st[0]), torch.zeros_like(st[0]),
+               torch.empty(u.S, dtype=torch.bfloat16, device=DEV)]
+        fsdp.reduce_adamw_shard(u, rows, *st, HPD, 1)
+        shards.append(st)
+    fsdp.reduce_adamw_shard(ddp, rows, *full, HPD, 1)
+    torch.cuda.synchronize()
+    for j in range(4):
+        cat = torch.cat([s[j] for s in shards])[:ddp.U]
+        a = cat.view(torch.int16 if cat.dtype == torch.bfloat16 else torch.int32)
+        b = full[j].view(torch.int16 if full[j].dtype == torch.bfloat16 else torch.int32)
+        assert torch.equal(a, b), j
