@@ -64,6 +64,18 @@
 #define FSDP_COPY_NT_STORE 0   // streaming hint on the copy kernels' 128-bit stores
 #endif
 
+// Resident step workgroups per CU (0: no cap). The cap is imposed with unused
+// dynamic LDS, a CU holding 160 KiB of it.
+#ifndef FSDP_REDUCE_WG_PER_CU
+#define FSDP_REDUCE_WG_PER_CU 0
+#endif
+#ifndef FSDP_ADAMW_WG_PER_CU
+#define FSDP_ADAMW_WG_PER_CU 3
+#endif
+#ifndef FSDP_FUSED_WG_PER_CU
+#define FSDP_FUSED_WG_PER_CU 0
+#endif
+
 using fsdp::fail;
 
 namespace {
@@ -663,16 +675,38 @@ fsdp_status after_launch(const char* what) {
   return FSDP_OK;
 }
 
+// The reservation is the largest 4 KiB multiple of which wg_per_cu fit in a
+// CU, so that allocation granules cannot round it up past that count.
+constexpr size_t kLdsPerCu = 160 * 1024;
+constexpr size_t lds_for_cap(int wg_per_cu) {
+  return wg_per_cu <= 0 ? 0 : (kLdsPerCu / wg_per_cu) / 4096 * 4096;
+}
+constexpr bool cap_exact(int wg_per_cu) {
+  return wg_per_cu <= 0 || (wg_per_cu + 1) * lds_for_cap(wg_per_cu) > kLdsPerCu;
+}
+static_assert(cap_exact(FSDP_REDUCE_WG_PER_CU) && cap_exact(FSDP_ADAMW_WG_PER_CU) &&
+                  cap_exact(FSDP_FUSED_WG_PER_CU),
+              "workgroup cap not representable by a 4 KiB LDS reservation");
+// LDS bytes a step workgroup reserves. The stand-alone AdamW kernel (four
+// fp32 streams in, three out) is faster with three workgroups per CU; the
+// reduce and fused kernels are faster at full occupancy.
+template <Op OP>
+constexpr size_t step_lds() {
+  return lds_for_cap(OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
+                     : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
+                                       : FSDP_FUSED_WG_PER_CU);
+}
+
 template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a);   // general fold
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a);   // general fold
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -683,7 +717,7 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
   }
   }
 }
@@ -692,7 +726,7 @@ template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -703,7 +737,7 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, 0, stream>>>(a); break;
+    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
   }
 }
 
