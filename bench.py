@@ -59,6 +59,101 @@ def read_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+def device_record():
+    """Marketing name, ISA, CU count and peak engine clock of GPU agent 0, from rocminfo.
+
+    Runs before this process touches the GPU."""
+    import subprocess
+    rec = {}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError) as e:
+        return {"error": f"rocminfo: {e}"}
+    for block in re.split(r"^\s*Agent \d+\s*$", out, flags=re.M)[1:]:
+        if not re.search(r"^\s*Device Type:\s*GPU\s*$", block, re.M):
+            continue
+        for key, name in (("Marketing Name", "marketing_name"), ("Name", "isa"),
+                          ("Compute Unit", "compute_units"),
+                          ("Max Clock Freq. (MHz)", "max_clock_mhz")):
+            m = re.search(r"^[ \t]*" + re.escape(key) + r":[ \t]*(.*?)[ \t]*$", block, re.M)
+            if m:
+                rec[name] = m.group(1)
+        break
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Host cores to use: the process's CPU set, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_worker(F: int, rank: int, first: int, n: int, budget_s: float):
+    """One worker of the all-cores oracle run: the fused oracle step on shard
+    elements [first, first + n), repeated for budget_s; prints its rate."""
+    import numpy as np
+
+    import datagen
+    from datagen import workloads as W
+    from oracle import fsdp_oracle as O
+
+    L = O.unit_layout(W.shapes(W.BLK7), F, rank)
+    g = L.shard_begin + first + np.arange(n, dtype=np.int64)
+    grads = [datagen.bf16_bits_host(datagen.seed_for(1, 1, 1), k, g, W.GRAD_SIGMA)
+             for k in range(F)]
+    p = datagen.normal_f32_host(datagen.seed_for(1, 0), 0, g, W.MASTER_SIGMA)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    one = O.unit_layout([(n,)], 1, 0)
+    hp = O.AdamW(**W.ADAMW)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.reduce_adamw_shard(grads, one, p, m, v, hp, 1, grad_scale=1.0 / F, emit_bf16=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= 2 and el >= budget_s:
+            break
+    print(json.dumps({"elements": n * reps, "seconds": el}), flush=True)
+
+
+def cpu_all_cores(F: int, rank: int, per_worker: int, budget_s: float):
+    """The oracle on every host core: one single-threaded worker process per
+    core, each on its own stretch of the shard, started together."""
+    import subprocess
+    from oracle import fsdp_oracle as O
+    from datagen import workloads as W
+
+    valid = O.unit_layout(W.shapes(W.BLK7), F, rank).shard_valid
+    k = cpu_workers()
+    n = max(1, min(per_worker, valid // k))
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker",
+                               str(F), str(rank), str(j * n), str(n), str(budget_s)],
+                              stdout=subprocess.PIPE, text=True, env=env) for j in range(k)]
+    rate = 0.0
+    for pr in procs:
+        out, _ = pr.communicate(timeout=budget_s * 10 + 120)
+        if pr.returncode != 0:
+            return None
+        r = json.loads(out.strip().splitlines()[-1])
+        rate += r["elements"] / r["seconds"]
+    return {"value": rate, "cores": k, "elements_per_worker": n}
+
+
 def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
     """The CPU oracle (as it stands) on the first `sample` elements of the shard."""
     import numpy as np
@@ -97,13 +192,40 @@ def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
                                     2.0)[0],
         "a6_bf16_round": rate(lambda: O.bf16_round_nearest_even(p), 2.0)[0],
     }
-    return {
+    allc = cpu_all_cores(F, rank, 1 << 20, budget_s)
+    per_param = 2 * F + 26
+    res = {
         "value": value, "unit": "params/s", "cores": 1, "kind": "oracle",
         "sample": (f"fused reduce+AdamW+bf16 emit of the CPU oracle (numpy, one thread) on the "
                    f"first {n:,} elements of rank {rank}'s shard of the 7B block at F={F}, "
                    f"{reps} repetitions, {el:.1f} s"),
+        "GBps": value * per_param / 1e9,
+        "cpu_model": cpu_model(),
         "rows_params_per_s": rows,
     }
+    if allc is not None:
+        res["all_cores"] = {
+            "value": allc["value"], "unit": "params/s", "cores": allc["cores"],
+            "GBps": allc["value"] * per_param / 1e9,
+            "sample": (f"the same oracle step in {allc['cores']} single-threaded processes at "
+                       f"once, each on its own {allc['elements_per_worker']:,} shard elements, "
+                       f"about {budget_s:.0f} s each"),
+        }
+    return res
+
+
+def spread(ms):
+    """Average, median, 10th and 90th percentile and minimum of event intervals, in us."""
+    xs = sorted(x * 1e3 for x in ms)
+
+    def pct(q):
+        i = q * (len(xs) - 1)
+        lo = int(i)
+        hi = min(lo + 1, len(xs) - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
+
+    return {"avg": sum(xs) / len(xs), "median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
+            "min": xs[0]}
 
 
 def rotating_rows(torch, datagen, W, unit, n_rows, n_sets, dev, seed, outlier_seed=None):
@@ -458,6 +580,10 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         pmc_summary(sys.argv[2], sys.argv[3])
         return
+    if len(sys.argv) > 1 and sys.argv[1] == "--cpu-worker":
+        F, rank, first, n = (int(x) for x in sys.argv[2:6])
+        cpu_worker(F, rank, first, n, float(sys.argv[6]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -479,6 +605,8 @@ def main():
               "supported (the cross-GPU exchange steps are not part of this build)",
               file=sys.stderr)
         sys.exit(2)
+
+    device = device_record() if args.workload == "blk7" else None
 
     import torch
 
@@ -571,6 +699,7 @@ def main():
     elapsed = time.perf_counter() - t0
     fused_ms = [a.elapsed_time(b) for a, b, _ in ev]
     gather_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ev_ms = [a.elapsed_time(c) for a, _, c in ev]
     fused_avg = sum(fused_ms) / K
     gather_avg = sum(gather_ms) / K
     ms_per_step = elapsed * 1e3 / K
@@ -619,6 +748,7 @@ def main():
     # counters also calibrate the HBM traffic figures)
     copy_gbps = copy_reference(fsdp, torch, dev, stream)
 
+    props = torch.cuda.get_device_properties(dev)
     fused_bytes = (2 * F + 26) * n                # bf16 rows + fp32 p/m/v in/out + bf16 out
     gather_bytes = 4 * u.U                        # bf16 in (F*S valid) + bf16 out
     achieved = fused_bytes / (fused_avg * 1e-3) / 1e9
@@ -661,7 +791,12 @@ def main():
         "step_GBps": (fused_bytes + gather_bytes) / (ms_per_step * 1e-3) / 1e9,
         "unit_params_per_s": u.U / (ms_per_step * 1e-3),
         "copy_GBps": copy_gbps,
+        "timing_us": {"fused": spread(fused_ms), "gather": spread(gather_ms),
+                      "step": spread(step_ev_ms)},
         "rows_alone": rows,
+        "device": dict(device or {}, torch_name=props.name, arch=props.gcnArchName,
+                       multiprocessors=props.multi_processor_count,
+                       hbm_bytes=props.total_memory),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

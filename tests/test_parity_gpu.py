@@ -346,6 +346,56 @@ def test_blk7_cast_unflatten_full_size_sampled():
         assert_bits(gather(o.reshape(-1), j), want, f"tensor {i}")
 
 
+def test_blk7_f8_every_rank_every_element(blk7_grads):
+    """The 7B block at F=8 in full: every rank's shard, every element, one
+    fused step with bf16 emission, then the gather of the eight emitted shards
+    into the nine tensors.
+
+    Inputs are the seeded generator's device fills, spot-checked here against
+    its host form; the expected values are the oracle's on host copies of
+    those fills."""
+    shapes, F = W.shapes(W.BLK7), 8
+    case0 = Case(shapes, F, 0, config=1)
+    grads = case0.device_grads(1, out=blk7_grads[:8])
+    masters = case0.device_master_tensors()
+    torch.cuda.synchronize()
+    U = case0.L.U
+    idx = np.unique(np.concatenate([np.random.default_rng(7).integers(0, U, 4096),
+                                    np.arange(8), U - 1 - np.arange(8)]))
+    for k in (0, F - 1):
+        assert_bits(gather(grads[k], idx), case0.host_grads_at(1, idx)[k], f"row {k} fill")
+    assert_bits(np.concatenate([to_np(t) for t in masters])[idx].view(np.uint32),
+                case0.host_master_at(idx).view(np.uint32), "master fill")
+    rows = [to_np(g) for g in grads]
+    flat = O.flatten_pad([to_np(t).view(np.uint32) for t in masters], F).view(np.float32)
+    emitted = []
+    for rank in range(F):
+        u = fsdp.Unit(shapes, F, rank)
+        p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+        fsdp.flatten_pad(u, masters, p)
+        m = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+        v = torch.zeros(u.S, dtype=torch.float32, device=DEV)
+        w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, 1)
+        torch.cuda.synchronize()
+        L = O.unit_layout(shapes, F, rank)
+        lo, hi = L.shard_begin, L.shard_begin + L.shard_valid
+        z = np.zeros(L.shard_valid, np.float32)
+        want = O.reduce_adamw_shard(rows, L, flat[lo:hi].copy(), z, z.copy(), HP, 1,
+                                    grad_scale=1.0 / F, emit_bf16=True)
+        fr = compare_full(Case(shapes, F, rank, config=1), (u, p, m, v, w), want)
+        log(f"rank {rank}: bit-equal fractions {fr}")
+        emitted.append(w)
+        del p, m, v
+    u = fsdp.Unit(shapes, F, 0)
+    outs = [torch.empty(sh, dtype=torch.bfloat16, device=DEV) for sh in shapes]
+    fsdp.cast_unflatten(u, emitted, outs)
+    torch.cuda.synchronize()
+    want = O.unflatten([to_np(w) for w in emitted], O.unit_layout(shapes, F, 0), shapes)
+    for i, (o, e) in enumerate(zip(outs, want)):
+        assert_bits(to_np(o).reshape(-1), np.asarray(e).reshape(-1), f"gathered tensor {i}")
+
+
 @pytest.mark.parametrize("F", [1, 2, 4, 8, 16, 64, 7, 11, 13])
 def test_blk7_sharding_factor_sweep_with_outliers_sampled(F, sweep_grads):
     for rank in sorted({0, F - 1}):
