@@ -398,11 +398,13 @@ def test_blk7_f8_every_rank_every_element(blk7_grads):
 
 @pytest.mark.parametrize("F", [1, 2, 4, 8, 16, 64, 7, 11, 13])
 def test_blk7_sharding_factor_sweep_with_outliers_sampled(F, sweep_grads):
-    for rank in sorted({0, F - 1}):
+    """Every rank of every sharding factor (ranks 0 and F-1 with more samples)."""
+    for rank in range(F):
         case = Case(W.shapes(W.BLK7), F, rank, config=3, outliers=True)
         log(f"sweep F={F} rank={rank} S={case.L.S} valid={case.L.shard_valid}")
         u, p, m, v, w = run_rank(case, 1, grads_buf=sweep_grads[:F], grads_ready=True)
-        loc = case.sample_indices(1 << 15, seed=F)
+        n = 1 << 15 if rank in (0, F - 1) else (1 << 15) // F
+        loc = case.sample_indices(n, seed=F * 64 + rank)
         want = case.oracle_sampled(loc, 1)[-1]
         assert_rel(gather(p, loc), want[0], what="master")
         assert_rel(gather(m, loc), want[1], what="exp_avg")
