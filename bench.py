@@ -228,15 +228,29 @@ def spread(ms):
             "min": xs[0]}
 
 
-def rotating_rows(torch, datagen, W, unit, n_rows, n_sets, dev, seed, outlier_seed=None):
+def rotating_rows(torch, datagen, W, unit, n_rows, n_sets, dev, seed, outlier_seed=None,
+                  separate=False):
     """n_sets sets of n_rows gradient rows whose rank windows are all disjoint.
 
-    The kernels read only [shard_begin, shard_begin + shard_valid) of a row, so
-    each row is a U-long view into one arena, placed so that its window lands
-    on its own stretch of the arena: R*n_rows*S elements are filled instead of
-    R*n_rows*U allocated.
+    The kernels read only [shard_begin, shard_begin + shard_valid) of a row.
+    separate=True: every row is its own U-element allocation (one buffer per
+    contributing rank, as the ranks' gradients are), only its window filled.
+    Otherwise each row is a U-long view into one arena, placed so that its
+    window lands on its own stretch of the arena: R*n_rows*S elements are
+    filled and allocated instead of R*n_rows*U allocated.
     """
     S, U, r0 = unit.S, unit.U, unit.shard_begin
+    if separate:
+        out = []
+        for j in range(n_sets):
+            rows = []
+            for k in range(n_rows):
+                row = torch.empty(U, dtype=torch.bfloat16, device=dev)
+                datagen.fill_bf16_(row[r0:r0 + unit.shard_valid], seed, 64 * j + k,
+                                   W.GRAD_SIGMA, start=r0, outlier_seed=outlier_seed)
+                rows.append(row)
+            out.append(rows)
+        return out
     S8 = (S + 7) // 8 * 8          # window spacing that keeps every row base 16-byte aligned
     arena = torch.empty(r0 + n_sets * n_rows * S8 + U, dtype=torch.bfloat16, device=dev)
     out = []
@@ -595,6 +609,8 @@ def main():
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
+    ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],
+                    help="blk7: one allocation per gradient row, or all rows' windows in one arena")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -642,7 +658,8 @@ def main():
     # ---- inputs resident in HBM: R independent sets, visited in turn -------
     # (every set has its own gradient windows, optimizer state, bf16 shards and
     # outputs, so no step finds the previous step's data in a cache)
-    row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1))
+    row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1),
+                             separate=args.row_layout == "separate")
     sets, set_masters = [], []
     for j in range(R):
         masters = []

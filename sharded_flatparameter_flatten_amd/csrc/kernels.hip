@@ -13,10 +13,14 @@
 //    gradient never touches memory;
 //  * cache policy, chosen by measurement on MI355X with rotating buffer sets
 //    (no reuse between steps): the gradient rows are read once, so their
-//    loads carry the streaming (nontemporal) hint, and so do all step-kernel
-//    stores; the fp32 state loads stay ordinary (the same lines are written
-//    back by the same wave); the copy kernels use ordinary loads and stores.
-//    This cut the 7B-block step (fused + gather) from ~331 us to ~318 us;
+//    loads carry the streaming (nontemporal) hint; the fp32 state loads stay
+//    ordinary; every vector store of the step and copy kernels is a
+//    device-scope streaming store (buffer store with sc1 nt) through a
+//    descriptor bounded to the workgroup's tile. With ordinary or plain
+//    nontemporal stores, part of a kernel's writes was still being written
+//    back while the next kernel ran and slowed it; the streaming stores
+//    finish inside the kernel that issues them, and the 7B-block step
+//    (fused + gather) went from ~318 us to ~307 us;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
@@ -57,11 +61,15 @@
 #ifndef FSDP_COPY_NT_LOAD
 #define FSDP_COPY_NT_LOAD 0    // streaming hint on the copy kernels' source loads
 #endif
-#ifndef FSDP_STEP_NT_STORE
-#define FSDP_STEP_NT_STORE 1   // streaming hint on the step kernels' 128-bit stores
+// Cache policy of the step and copy kernels' vector stores: the CPol operand
+// of the gfx950 buffer store (1 = sc0, 2 = nt, 16 = sc1). The default, 18, is a
+// device-scope streaming store (sc1 nt). -1 selects plain global stores
+// instead (with the nontemporal hint on the step kernels).
+#ifndef FSDP_STEP_STORE_CPOL
+#define FSDP_STEP_STORE_CPOL 18
 #endif
-#ifndef FSDP_COPY_NT_STORE
-#define FSDP_COPY_NT_STORE 0   // streaming hint on the copy kernels' 128-bit stores
+#ifndef FSDP_COPY_STORE_CPOL
+#define FSDP_COPY_STORE_CPOL 18
 #endif
 
 // Resident step workgroups per CU (0: no cap). The cap is imposed with unused
@@ -142,8 +150,8 @@ __device__ __forceinline__ void st(void* p, V x) {
   if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<V*>(p));
   else *reinterpret_cast<V*>(p) = x;
 }
-constexpr bool kStepNt = FSDP_STEP_NT_STORE != 0;
-constexpr bool kCopyNt = FSDP_COPY_NT_STORE != 0;
+constexpr int kStepCpol = FSDP_STEP_STORE_CPOL;
+constexpr int kCopyCpol = FSDP_COPY_STORE_CPOL;
 constexpr bool kGradNt = FSDP_GRAD_NT_LOAD != 0;
 constexpr bool kCopyNtLoad = FSDP_COPY_NT_LOAD != 0;
 constexpr bool kStateNt = FSDP_STATE_NT_LOAD != 0;
@@ -167,16 +175,37 @@ __device__ __forceinline__ void loadf(const float* p, float (&x)[SV]) {
     x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
   }
 }
-template <int SV, bool NT>
-__device__ __forceinline__ void storef(float* p, const float (&x)[SV]) {
-#pragma unroll
-  for (int h = 0; h < SV / 4; ++h)
-    st<f32x4, NT>(p + 4 * h, f32x4{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]});
+
+// Buffer descriptor over [base, base + bytes) with the gfx9 raw-buffer format
+// word; a store beyond it is dropped by the hardware.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, static_cast<int>(bytes), kRsrcWord3);
 }
-template <int SV, bool NT>
-__device__ __forceinline__ void store_bf16(uint16_t* p, const float (&x)[SV]) {
-  static_assert(SV == 4, "4 elements per lane");
-  st<u32x2, NT>(p, u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])});
+template <int CP>
+__device__ __forceinline__ void bst(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void bst(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CP);
+}
+
+// One lane's 4 results at element i of a workgroup tile that starts at
+// element t0 of `base` and holds `len` elements (all workgroup-uniform but i).
+// Each store is a single 16-byte (fp32) or 8-byte (bf16) access.
+__device__ __forceinline__ void out_f32(float* base, int64_t t0, int64_t len, int64_t i,
+                                        const float (&x)[4]) {
+  const u32x4 b = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                   __float_as_uint(x[3])};
+  if constexpr (kStepCpol >= 0) bst<kStepCpol>(rsrc(base + t0, 4 * len), int(4 * (i - t0)), b);
+  else st<u32x4, true>(base + i, b);
+}
+__device__ __forceinline__ void out_bf16(uint16_t* base, int64_t t0, int64_t len, int64_t i,
+                                         const float (&x)[4]) {
+  const u32x2 b = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+  if constexpr (kStepCpol >= 0) bst<kStepCpol>(rsrc(base + t0, 2 * len), int(2 * (i - t0)), b);
+  else st<u32x2, true>(base + i, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -380,8 +409,11 @@ template <Op OP, int NG, bool EMIT>
 __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * kStepTile;
-  for (int64_t i = int64_t(blockIdx.x) * kStepTile + int64_t(threadIdx.x) * kSV; i < n;
-       i += stride) {
+  for (int64_t t0 = int64_t(blockIdx.x) * kStepTile; t0 < n; t0 += stride) {
+    // t0, this tile's first element, is workgroup-uniform (the store descriptors
+    // are built from it in scalar registers)
+    const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
+    if (i >= n) continue;
     if (i + kSV <= n) {
       float g[kSV];
       if constexpr (OP == Op::AdamW) {
@@ -398,8 +430,9 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
           reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
         }
       }
+      const int64_t tl = n - t0 < kStepTile ? n - t0 : int64_t(kStepTile);
       if constexpr (OP == Op::Reduce) {
-        storef<kSV, kStepNt>(a.out + i, g);
+        out_f32(a.out, t0, tl, i, g);
       } else {
         float p[kSV], m[kSV], v[kSV];
         loadf<kSV>(a.p + i, p);
@@ -407,10 +440,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
         loadf<kSV>(a.v + i, v);
 #pragma unroll
         for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
-        storef<kSV, kStepNt>(a.p + i, p);
-        storef<kSV, kStepNt>(a.m + i, m);
-        storef<kSV, kStepNt>(a.v + i, v);
-        if constexpr (EMIT) store_bf16<kSV, kStepNt>(a.w + i, p);
+        out_f32(a.p, t0, tl, i, p);
+        out_f32(a.m, t0, tl, i, m);
+        out_f32(a.v, t0, tl, i, v);
+        if constexpr (EMIT) out_bf16(a.w, t0, tl, i, p);
       }
     } else {
       for (int64_t j = i; j < n; ++j) step_scalar<OP>(a, j);
@@ -429,12 +462,15 @@ __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   constexpr int64_t TILE = int64_t(kStepThreads) * V;
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * TILE;
-  for (int64_t i = int64_t(blockIdx.x) * TILE + int64_t(threadIdx.x) * V; i < n; i += stride) {
+  for (int64_t t0 = int64_t(blockIdx.x) * TILE; t0 < n; t0 += stride) {
+    const int64_t i = t0 + int64_t(threadIdx.x) * V;     // t0 is workgroup-uniform
+    if (i >= n) continue;
     if (i >= V && i + 2 * V <= n) {
       float g[V];
       reduce_rows_shifted<NG>(a, i, g);
+      const int64_t tl = n - t0 < TILE ? n - t0 : TILE;
       if constexpr (OP == Op::Reduce) {
-        storef<V, kStepNt>(a.out + i, g);
+        out_f32(a.out, t0, tl, i, g);
       } else {
         float p[V], m[V], v[V];
         loadf<V>(a.p + i, p);
@@ -442,10 +478,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
         loadf<V>(a.v + i, v);
 #pragma unroll
         for (int e = 0; e < V; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
-        storef<V, kStepNt>(a.p + i, p);
-        storef<V, kStepNt>(a.m + i, m);
-        storef<V, kStepNt>(a.v + i, v);
-        if constexpr (EMIT) store_bf16<V, kStepNt>(a.w + i, p);
+        out_f32(a.p, t0, tl, i, p);
+        out_f32(a.m, t0, tl, i, m);
+        out_f32(a.v, t0, tl, i, v);
+        if constexpr (EMIT) out_bf16(a.w, t0, tl, i, p);
       }
     } else {
       const int64_t end = i + V < n ? i + V : n;
@@ -521,8 +557,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_multi(MultiArgs a) {
     const int s = find_entry(a.u, a.nu, t);
     const int64_t tile0 = s == 0 ? 0 : a.u[s - 1].tile_end;
     const UnitDesc& d = a.u[s];
-    const int64_t i = (t - tile0) * kStepTile + int64_t(threadIdx.x) * kSV;
+    const int64_t t0 = (t - tile0) * kStepTile;              // this tile's first element
+    const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
     if (i + kSV <= d.n) {
+      const int64_t tl = d.n - t0 < kStepTile ? d.n - t0 : int64_t(kStepTile);
       float g[kSV], p[kSV], m[kSV], v[kSV];
       reduce_rows<NG, kSV>(d.g, a.n_grads, a.s.gs, i, g);
       loadf<kSV>(d.p + i, p);
@@ -530,10 +568,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_multi(MultiArgs a) {
       loadf<kSV>(d.v + i, v);
 #pragma unroll
       for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
-      storef<kSV, kStepNt>(d.p + i, p);
-      storef<kSV, kStepNt>(d.m + i, m);
-      storef<kSV, kStepNt>(d.v + i, v);
-      if (d.w) store_bf16<kSV, kStepNt>(d.w + i, p);
+      out_f32(d.p, t0, tl, i, p);
+      out_f32(d.m, t0, tl, i, m);
+      out_f32(d.v, t0, tl, i, v);
+      if (d.w) out_bf16(d.w, t0, tl, i, p);
     } else {
       for (int64_t j = i; j < d.n; ++j) fused_scalar(d.g, a.n_grads, d.p, d.m, d.v, d.w, j, a.s);
     }
@@ -577,10 +615,8 @@ struct CopyKind<0> {
   using D = uint32_t;
   static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return x; }
-  static __device__ __forceinline__ void vec(const S* s, D* d) {
-    st<u32x4, kCopyNt>(d, ldh<u32x4, kCopyNtLoad>(s));
-  }
-  static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
+  using V = u32x4;
+  static __device__ __forceinline__ V bits(const S* s) { return ldh<u32x4, kCopyNtLoad>(s); }
 };
 template <>
 struct CopyKind<1> {
@@ -588,10 +624,8 @@ struct CopyKind<1> {
   using D = uint16_t;
   static constexpr int EPL = 8;
   static __device__ __forceinline__ D cvt(S x) { return x; }
-  static __device__ __forceinline__ void vec(const S* s, D* d) {
-    st<u32x4, kCopyNt>(d, ldh<u32x4, kCopyNtLoad>(s));
-  }
-  static __device__ __forceinline__ void zero(D* d) { st<u32x4, kCopyNt>(d, u32x4{0u, 0u, 0u, 0u}); }
+  using V = u32x4;
+  static __device__ __forceinline__ V bits(const S* s) { return ldh<u32x4, kCopyNtLoad>(s); }
 };
 template <>
 struct CopyKind<2> {
@@ -599,11 +633,11 @@ struct CopyKind<2> {
   using D = uint16_t;
   static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return static_cast<uint16_t>(to_bf16(x)); }
-  static __device__ __forceinline__ void vec(const S* s, D* d) {
+  using V = u32x2;
+  static __device__ __forceinline__ V bits(const S* s) {
     const f32x4 x = ldh<f32x4, kCopyNtLoad>(s);
-    st<u32x2, kCopyNt>(d, u32x2{pack_bf16(x.x, x.y), pack_bf16(x.z, x.w)});
+    return V{pack_bf16(x.x, x.y), pack_bf16(x.z, x.w)};
   }
-  static __device__ __forceinline__ void zero(D* d) { st<u32x2, kCopyNt>(d, u32x2{0u, 0u}); }
 };
 
 template <>
@@ -612,12 +646,11 @@ struct CopyKind<3> {
   using D = float;
   static constexpr int EPL = 4;
   static __device__ __forceinline__ D cvt(S x) { return widen(x); }
-  static __device__ __forceinline__ void vec(const S* s, D* d) {
+  using V = u32x4;
+  static __device__ __forceinline__ V bits(const S* s) {
     const u32x2 q = ldh<u32x2, kCopyNtLoad>(s);
-    st<f32x4, kCopyNt>(d, f32x4{lo_bf16(q.x), hi_bf16(q.x), lo_bf16(q.y), hi_bf16(q.y)});
-  }
-  static __device__ __forceinline__ void zero(D* d) {
-    st<f32x4, kCopyNt>(d, f32x4{0.f, 0.f, 0.f, 0.f});
+    return V{__float_as_uint(lo_bf16(q.x)), __float_as_uint(hi_bf16(q.x)),
+             __float_as_uint(lo_bf16(q.y)), __float_as_uint(hi_bf16(q.y))};
   }
 };
 
@@ -643,8 +676,14 @@ __global__ __launch_bounds__(kThreads) void k_segcopy(SegArgs a) {
     if (mode == kSegVec || mode == kSegZeroVec) {
       const int64_t i = base + int64_t(threadIdx.x) * EPL;
       if (i + EPL <= len) {
-        if (mode == kSegVec) K::vec(src + i, dst + i);
-        else K::zero(dst + i);
+        const typename K::V x = mode == kSegVec ? K::bits(src + i) : typename K::V{};
+        if constexpr (kCopyCpol >= 0) {
+          const int64_t tl = len - base < TILE ? len - base : TILE;
+          bst<kCopyCpol>(rsrc(dst + base, tl * int64_t(sizeof(D))),
+                         int(threadIdx.x) * EPL * int(sizeof(D)), x);
+        } else {
+          st<typename K::V, false>(dst + i, x);
+        }
       } else {
         for (int64_t j = i; j < len; ++j) dst[j] = mode == kSegVec ? K::cvt(src[j]) : D(0);
       }
