@@ -308,24 +308,39 @@ def model_sequence(args):
     v = torch.zeros(total, dtype=torch.float32, device=dev)
     w = torch.empty(total, dtype=torch.bfloat16, device=dev)
     gseed = datagen.seed_for(wl["config"], 1, 1)
+    # Gradient rows: `row_sets` sets of F rows per distinct unit size, unit i of
+    # that size using set i % row_sets, so that consecutive units never read the
+    # same rows (a unit's rows are re-read only after other units' traffic has
+    # gone through the memory-side cache). Only the rank windows are filled.
     arenas = {}
-    for u in units:                      # one set of rows per distinct unit size
+    for u in units:
         if u.U not in arenas:
-            rows = [torch.empty(u.U, dtype=torch.bfloat16, device=dev) for _ in range(F)]
-            for k in range(F):
-                datagen.fill_bf16_(rows[k], gseed, 100 * len(arenas) + k, W.GRAD_SIGMA)
-            arenas[u.U] = rows
+            sets = []
+            for j in range(args.row_sets):
+                rows = [torch.empty(u.U, dtype=torch.bfloat16, device=dev) for _ in range(F)]
+                for k in range(F):
+                    datagen.fill_bf16_(rows[k][u.shard_begin:u.shard_begin + u.shard_valid],
+                                       gseed, 100 * len(arenas) + 16 * j + k, W.GRAD_SIGMA,
+                                       start=u.shard_begin)
+                sets.append(rows)
+            arenas[u.U] = sets
+    seen = {}
+    unit_rows = []
+    for u in units:
+        j = seen.get(u.U, 0)
+        seen[u.U] = j + 1
+        unit_rows.append(arenas[u.U][j % args.row_sets])
     hp = fsdp.AdamWHparams(**W.ADAMW)
     stream = torch.cuda.current_stream(dev)
     win = [(p[a:a + u.S], m[a:a + u.S], v[a:a + u.S], w[a:a + u.S])
            for u, a in zip(units, starts)]
 
-    batch = [(u, arenas[u.U]) + tuple(wn) for u, wn in zip(units, win)]
+    batch = [(u, rows) + tuple(wn) for u, rows, wn in zip(units, unit_rows, win)]
 
     def step(t):
         if args.per_unit:
-            for u, (pp, mm, vv, ww) in zip(units, win):
-                fsdp.reduce_adamw_shard(u, arenas[u.U], pp, mm, vv, ww, hp, t, stream=stream)
+            for u, rows, (pp, mm, vv, ww) in zip(units, unit_rows, win):
+                fsdp.reduce_adamw_shard(u, rows, pp, mm, vv, ww, hp, t, stream=stream)
         else:
             fsdp.reduce_adamw_units(batch, hp, t, stream=stream)
 
@@ -348,7 +363,7 @@ def model_sequence(args):
         "metric": "model shard step params/s + HBM GB/s", "workload": args.workload,
         "value": valid / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_step, "wall_ms_per_step": elapsed * 1e3 / K,
-        "units": len(units), "shard_params": valid,
+        "units": len(units), "shard_params": valid, "row_sets": args.row_sets,
         "entry_point": "fsdp_reduce_adamw_shard per unit" if args.per_unit
         else "fsdp_reduce_adamw_units (batched launches)",
         "persistent_bytes": sum(u.persistent_bytes for u in units),
@@ -607,6 +622,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
+    ap.add_argument("--row-sets", type=int, default=2,
+                    help="whole-model workloads: gradient row sets per unit size, used in turn")
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],

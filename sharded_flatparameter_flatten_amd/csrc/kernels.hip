@@ -81,7 +81,7 @@
 #define FSDP_ADAMW_WG_PER_CU 3
 #endif
 #ifndef FSDP_FUSED_WG_PER_CU
-#define FSDP_FUSED_WG_PER_CU 0
+#define FSDP_FUSED_WG_PER_CU 3
 #endif
 
 using fsdp::fail;
@@ -726,26 +726,30 @@ constexpr bool cap_exact(int wg_per_cu) {
 static_assert(cap_exact(FSDP_REDUCE_WG_PER_CU) && cap_exact(FSDP_ADAMW_WG_PER_CU) &&
                   cap_exact(FSDP_FUSED_WG_PER_CU),
               "workgroup cap not representable by a 4 KiB LDS reservation");
-// LDS bytes a step workgroup reserves. The stand-alone AdamW kernel (four
-// fp32 streams in, three out) is faster with three workgroups per CU; the
-// reduce and fused kernels are faster at full occupancy.
-template <Op OP>
+// LDS bytes a step workgroup reserves. With the streaming stores, the
+// stand-alone AdamW kernel and the fused kernels with a compile-time row count
+// (all row loads in flight at once) are fastest with three workgroups per CU.
+// The fused kernels that walk a run-time row count in dependent chunks (other
+// counts, hybrid groups, bf16 partials) need every wave and stay uncapped, as
+// does the reduce-only kernel.
+template <Op OP, int NG>
 constexpr size_t step_lds() {
   return lds_for_cap(OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
                      : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
-                                       : FSDP_FUSED_WG_PER_CU);
+                     : NG > 0          ? FSDP_FUSED_WG_PER_CU
+                                       : 0);
 }
 
 template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a);   // general fold
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a);   // general fold
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP, K>(), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -756,7 +760,7 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a); break;
   }
   }
 }
@@ -765,7 +769,7 @@ template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
+  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP, K>(), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -776,7 +780,7 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP>(), stream>>>(a); break;
+    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a); break;
   }
 }
 
