@@ -302,11 +302,26 @@ def model_sequence(args):
     total = starts[-1]
     print(f"# workload {args.workload}: {len(units)} units, shard {total:,} params", file=sys.stderr,
           flush=True)
-    p = torch.empty(total, dtype=torch.float32, device=dev)
-    datagen.fill_normal_f32_(p, datagen.seed_for(wl["config"], 0), 0, W.MASTER_SIGMA)
-    m = torch.zeros(total, dtype=torch.float32, device=dev)
-    v = torch.zeros(total, dtype=torch.float32, device=dev)
-    w = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    # Optimizer state: by default every unit's fp32 master / m / v and bf16
+    # parameter shard are windows side by side in one allocation per array (one
+    # flat state buffer per rank); --state-layout per-unit gives each unit's
+    # arrays their own allocations instead.
+    mseed = datagen.seed_for(wl["config"], 0)
+    if args.state_layout == "packed":
+        p = torch.empty(total, dtype=torch.float32, device=dev)
+        datagen.fill_normal_f32_(p, mseed, 0, W.MASTER_SIGMA)
+        m = torch.zeros(total, dtype=torch.float32, device=dev)
+        v = torch.zeros(total, dtype=torch.float32, device=dev)
+        w = torch.empty(total, dtype=torch.bfloat16, device=dev)
+        win = [(p[a:a + u.S], m[a:a + u.S], v[a:a + u.S], w[a:a + u.S])
+               for u, a in zip(units, starts)]
+    else:
+        win = []
+        for i, u in enumerate(units):
+            pu = torch.empty(u.S, dtype=torch.float32, device=dev)
+            datagen.fill_normal_f32_(pu, mseed, i, W.MASTER_SIGMA)
+            win.append((pu, torch.zeros_like(pu), torch.zeros_like(pu),
+                        torch.empty(u.S, dtype=torch.bfloat16, device=dev)))
     gseed = datagen.seed_for(wl["config"], 1, 1)
     # Gradient rows: `row_sets` sets of F rows per distinct unit size, unit i of
     # that size using set i % row_sets, so that consecutive units never read the
@@ -332,8 +347,6 @@ def model_sequence(args):
         unit_rows.append(arenas[u.U][j % args.row_sets])
     hp = fsdp.AdamWHparams(**W.ADAMW)
     stream = torch.cuda.current_stream(dev)
-    win = [(p[a:a + u.S], m[a:a + u.S], v[a:a + u.S], w[a:a + u.S])
-           for u, a in zip(units, starts)]
 
     batch = [(u, rows) + tuple(wn) for u, rows, wn in zip(units, unit_rows, win)]
 
@@ -364,6 +377,7 @@ def model_sequence(args):
         "value": valid / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_step, "wall_ms_per_step": elapsed * 1e3 / K,
         "units": len(units), "shard_params": valid, "row_sets": args.row_sets,
+        "state_layout": args.state_layout,
         "entry_point": "fsdp_reduce_adamw_shard per unit" if args.per_unit
         else "fsdp_reduce_adamw_units (batched launches)",
         "persistent_bytes": sum(u.persistent_bytes for u in units),
@@ -624,6 +638,9 @@ def main():
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
     ap.add_argument("--row-sets", type=int, default=2,
                     help="whole-model workloads: gradient row sets per unit size, used in turn")
+    ap.add_argument("--state-layout", default="packed", choices=["packed", "per-unit"],
+                    help="whole-model workloads: all units' master/m/v/param windows packed into "
+                         "one allocation per array, or each unit's arrays allocated on their own")
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],
