@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -579,7 +580,6 @@ def _per_dispatch(rows, match, counter):
 def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
     """Prints the traffic summary (markdown + JSON block) from two rocprofv3 --pmc runs."""
     import datagen.workloads as W
-    from oracle import fsdp_oracle as O
 
     fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true>" % F)
     is_fused = lambda r: bool(fused.search(r.get("Kernel_Name", "")))
@@ -600,11 +600,12 @@ def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
     kw = cal_bytes / (avg(w_copy) * 1024)
     rd = avg(f_fused) * 1024 * kf
     wt = avg(w_fused) * 1024 * kw
-    L = O.unit_layout(W.shapes(W.BLK7), F, 0)
-    alg_r, alg_w = (2 * F + 12) * L.shard_valid, 14 * L.shard_valid
+    U = sum(math.prod(sh) for sh in W.shapes(W.BLK7))
+    valid = min(-(-U // F), U)                    # rank 0's shard: ceil(U / F) elements
+    alg_r, alg_w = (2 * F + 12) * valid, 14 * valid
     rec = {
         "kernel": "k_step_vec<Fused, %d, emit> (fused reduce+AdamW+bf16 emit)" % F,
-        "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, L.shard_valid),
+        "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, valid),
         "kernels_hip_sha256_16": kernel_source_hash(),
         "fused_dispatches": [len(f_fused), len(w_fused)],
         "fetch_kib_per_dispatch": avg(f_fused), "write_kib_per_dispatch": avg(w_fused),

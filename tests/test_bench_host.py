@@ -1,0 +1,95 @@
+"""CPU checks of bench.py's host-side logic (no GPU): the one-GPU guard, the
+timing spread, the rocminfo device record, the counter-summary gate and the
+all-cores oracle worker."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2" in r.stderr and "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_spread_percentiles_and_units():
+    s = bench.spread([i * 1e-3 for i in range(1, 11)])       # 1..10 us, given in ms
+    assert s["min"] == pytest.approx(1.0)
+    assert s["avg"] == pytest.approx(5.5)
+    assert s["median"] == pytest.approx(5.5)
+    assert s["p10"] == pytest.approx(1.9)
+    assert s["p90"] == pytest.approx(9.1)
+    one = bench.spread([0.25])
+    assert one["p10"] == one["p90"] == one["median"] == pytest.approx(250.0)
+
+
+ROCMINFO = """*******
+Agent 1
+*******
+  Name:                    Some CPU
+  Marketing Name:          Some CPU
+  Device Type:             CPU
+  Compute Unit:            128
+*******
+Agent 2
+*******
+  Name:                    gfx950
+  Uuid:                    GPU-0000
+  Marketing Name:          
+  Vendor Name:             AMD
+  Device Type:             GPU
+  Max Clock Freq. (MHz):   2400
+  Compute Unit:            256
+"""
+
+
+def test_device_record_reads_the_first_gpu_agent(monkeypatch):
+    class R:
+        stdout = ROCMINFO
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R)
+    rec = bench.device_record()
+    assert rec == {"marketing_name": "", "isa": "gfx950", "compute_units": "256",
+                   "max_clock_mhz": "2400"}
+
+
+def test_device_record_reports_a_missing_tool(monkeypatch):
+    def boom(*a, **k):
+        raise FileNotFoundError("rocminfo")
+    monkeypatch.setattr(subprocess, "run", boom)
+    assert "error" in bench.device_record()
+
+
+def test_traffic_figure_is_dropped_once_the_kernel_source_changes(tmp_path, monkeypatch):
+    src = tmp_path / "kernels.hip"
+    src.write_text("// kernel source\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    rec = {"kernels_hip_sha256_16": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123.0}
+    summary = tmp_path / "traffic.md"
+    summary.write_text("# traffic\n\n```json\n" + json.dumps(rec) + "\n```\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(summary))
+    assert bench.read_traffic() == 123.0
+    src.write_text("// kernel source, edited\n")
+    assert bench.read_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.md"))
+    assert bench.read_traffic() is None
+
+
+def test_cpu_worker_reports_its_rate():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--cpu-worker",
+                        "8", "0", "4096", "2048", "0.05"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    rec = json.loads(r.stdout.strip().splitlines()[-1])
+    assert rec["elements"] >= 2 * 2048 and rec["elements"] % 2048 == 0
+    assert rec["seconds"] > 0
