@@ -71,6 +71,24 @@ def test_indexer_brute_force(lib):
         _check_unit(shapes, F, int(rng.integers(0, F)), lib)
 
 
+def test_tensor_count_limit(lib):
+    """FSDP_MAX_TENSORS tensors (ragged, some empty) index like the oracle;
+    one more is rejected; so are more than 16 dimensions."""
+    rng = np.random.default_rng(5)
+    sizes = rng.integers(0, 9, 65536)
+    sizes[0] = 3
+    shapes = [(int(n),) for n in sizes]
+    for F, r in ((8, 0), (8, 7), (13, 6)):
+        _check_unit(shapes, F, r, lib)
+    with pytest.raises(lib.FsdpError) as e:
+        lib.Unit(shapes + [(1,)], 8, 0)
+    assert e.value.status == 1
+    lib.Unit([tuple([1] * 16)], 2, 0)
+    with pytest.raises(lib.FsdpError) as e:
+        lib.Unit([tuple([1] * 17)], 2, 0)
+    assert e.value.status == 1
+
+
 def test_config_totals_closed_form(lib):
     # one rank's persistent bytes for the 7B and 70B shapes at F=8
     blk7, root7 = lib.Unit(W.shapes(W.BLK7), 8, 0), lib.Unit(W.shapes(W.ROOT7), 8, 0)

@@ -199,6 +199,38 @@ def test_round_trip_flatten_then_unflatten_is_identity():
             assert_bits(to_np(o).reshape(-1), h, f"F={F}")
 
 
+def test_max_tensor_count_flatten_and_gather_bit_exact():
+    """FSDP_MAX_TENSORS ragged tensors (0..8 elements each, many empty, most
+    not 16-byte aligned), views into one buffer: every rank's fp32 flatten/pad
+    and the gather of the F shards back to bf16 tensors, against the oracle."""
+    rng = np.random.default_rng(11)
+    sizes = rng.integers(0, 9, 65536)
+    sizes[0] = 3
+    shapes = [(int(n),) for n in sizes]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    U, F = int(offs[-1]), 8
+    host = (rng.standard_normal(U) * 0.02).astype(np.float32)
+    src = torch.from_numpy(host).to(DEV)
+    tensors = [src[offs[i]:offs[i + 1]] for i in range(sizes.size)]
+    units = [fsdp.Unit(shapes, F, r) for r in range(F)]
+    shards = []
+    for u in units:
+        d = torch.empty(u.S, dtype=torch.float32, device=DEV)
+        fsdp.flatten_pad(u, tensors, d)
+        shards.append(d)
+    out = torch.empty(U, dtype=torch.bfloat16, device=DEV)
+    outs = [out[offs[i]:offs[i + 1]] for i in range(sizes.size)]
+    fsdp.cast_unflatten(units[0], shards, outs)
+    torch.cuda.synchronize()
+    L = O.unit_layout(shapes, F, 0)
+    flat = O.flatten_pad([host[offs[i]:offs[i + 1]].view(np.uint32) for i in range(sizes.size)], F)
+    S = L.S
+    for r in range(F):
+        assert_bits(to_np(shards[r]).view(np.uint32), flat[r * S:(r + 1) * S], f"shard {r}")
+    want = O.cast_unflatten([flat.view(np.float32)[r * S:(r + 1) * S] for r in range(F)], L, shapes)
+    assert_bits(to_np(out), np.concatenate([np.asarray(w).reshape(-1) for w in want]), "gather")
+
+
 # ---------------------------------------------------------------------------
 # ragged, padded, misaligned, many contributions (every element)
 # ---------------------------------------------------------------------------
