@@ -603,6 +603,22 @@ def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
     U = sum(math.prod(sh) for sh in W.shapes(W.BLK7))
     valid = min(-(-U // F), U)                    # rank 0's shard: ceil(U / F) elements
     alg_r, alg_w = (2 * F + 12) * valid, 14 * valid
+    # the gathers: the bf16 copies that move a whole unit (the init-time
+    # flattens of single shards are an F-th of that)
+    is_gather = lambda r: "k_segcopy<1>" in r.get("Kernel_Name", "")
+    f_g = largest(_per_dispatch(fr, is_gather, "FETCH_SIZE"))
+    w_g = largest(_per_dispatch(wr, is_gather, "WRITE_SIZE"))
+    gather = None
+    if f_g and w_g:
+        g_rd, g_wt = avg(f_g) * 1024 * kf, avg(w_g) * 1024 * kw
+        gather = {
+            "kernel": "k_segcopy<1> (fsdp_cast_unflatten, %d bf16 shards -> 9 tensors)" % F,
+            "dispatches": [len(f_g), len(w_g)],
+            "fetch_kib_per_dispatch": avg(f_g), "write_kib_per_dispatch": avg(w_g),
+            "hbm_read_bytes_per_launch": g_rd, "hbm_write_bytes_per_launch": g_wt,
+            "algorithmic_read_bytes": 2 * U, "algorithmic_write_bytes": 2 * U,
+            "traffic_over_algorithmic": (g_rd + g_wt) / (4 * U),
+        }
     rec = {
         "kernel": "k_step_vec<Fused, %d, emit> (fused reduce+AdamW+bf16 emit)" % F,
         "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, valid),
@@ -616,6 +632,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
         "hbm_bytes_per_launch": rd + wt,
         "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
         "traffic_over_algorithmic": (rd + wt) / (alg_r + alg_w),
+        "gather": gather,
     }
     print("```json\n" + json.dumps(rec, indent=1) + "\n```")
 
