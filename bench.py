@@ -647,8 +647,8 @@ def main():
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--F", type=int, default=8)
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=4,
@@ -752,23 +752,26 @@ def main():
         gather(i)
     torch.cuda.synchronize()
 
+    # Two timing events per step: `mid[i]` between the fused kernel and the
+    # gather, `edge[i + 1]` after the gather (which is also where step i + 1's
+    # fused kernel starts). Each event costs the stream a few microseconds, so
+    # no more are recorded than needed to time every launch.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    edge = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    edge[0].record(stream)
     for i in range(K):
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
         fused(W0 + i)
-        e1.record(stream)
+        mid[i].record(stream)
         gather(W0 + i)
-        e2.record(stream)
+        edge[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fused_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    gather_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ev_ms = [a.elapsed_time(c) for a, _, c in ev]
+    fused_ms = [edge[i].elapsed_time(mid[i]) for i in range(K)]
+    gather_ms = [mid[i].elapsed_time(edge[i + 1]) for i in range(K)]
+    step_ev_ms = [edge[i].elapsed_time(edge[i + 1]) for i in range(K)]
     fused_avg = sum(fused_ms) / K
     gather_avg = sum(gather_ms) / K
     ms_per_step = elapsed * 1e3 / K
@@ -792,7 +795,7 @@ def main():
         return {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
                 "frac_of_8TBps": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
 
-    reps = max(2 * R, args.steps // 2)
+    reps = max(2 * R, min(args.steps // 2, 48))
     rows = {
         "a2_flatten_pad_fp32": row("flatten", timed(lambda i: fsdp.flatten_pad(
             u, set_masters[i % R], flat_dst[i % R], stream=stream), reps), 8 * S),
