@@ -73,7 +73,9 @@
 #endif
 
 // Resident step workgroups per CU (0: no cap). The cap is imposed with unused
-// dynamic LDS, a CU holding 160 KiB of it.
+// dynamic LDS, a CU holding 160 KiB of it, and only on launches of at least
+// FSDP_CAP_MIN_TILES workgroups: a shorter launch has fewer tiles than a few
+// rounds of a full machine and runs best with every workgroup resident.
 #ifndef FSDP_REDUCE_WG_PER_CU
 #define FSDP_REDUCE_WG_PER_CU 0
 #endif
@@ -82,6 +84,12 @@
 #endif
 #ifndef FSDP_FUSED_WG_PER_CU
 #define FSDP_FUSED_WG_PER_CU 3
+#endif
+#ifndef FSDP_MULTI_WG_PER_CU
+#define FSDP_MULTI_WG_PER_CU 3    // the batched many-unit fused kernel
+#endif
+#ifndef FSDP_CAP_MIN_TILES
+#define FSDP_CAP_MIN_TILES 8192
 #endif
 
 using fsdp::fail;
@@ -514,6 +522,7 @@ constexpr int kMaxMultiUnits = 30;   // descriptors per launch (kernel arguments
 // Units at least this long get a launch of their own: there the per-launch
 // cost is negligible and the single-unit kernel, whose pointers sit at fixed
 // kernel-argument offsets, starts its workgroups sooner.
+// Units with fewer shard elements than this go through the batched kernel.
 constexpr int64_t kBatchMaxElems = int64_t(1) << 22;
 
 struct UnitDesc {
@@ -724,7 +733,7 @@ constexpr bool cap_exact(int wg_per_cu) {
   return wg_per_cu <= 0 || (wg_per_cu + 1) * lds_for_cap(wg_per_cu) > kLdsPerCu;
 }
 static_assert(cap_exact(FSDP_REDUCE_WG_PER_CU) && cap_exact(FSDP_ADAMW_WG_PER_CU) &&
-                  cap_exact(FSDP_FUSED_WG_PER_CU),
+                  cap_exact(FSDP_FUSED_WG_PER_CU) && cap_exact(FSDP_MULTI_WG_PER_CU),
               "workgroup cap not representable by a 4 KiB LDS reservation");
 // LDS bytes a step workgroup reserves. With the streaming stores, the
 // stand-alone AdamW kernel and the fused kernels with a compile-time row count
@@ -742,14 +751,15 @@ constexpr size_t step_lds() {
 
 template <Op OP, bool EMIT>
 void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
+  const bool cap = grid >= FSDP_CAP_MIN_TILES;
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a);   // general fold
+    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);   // general fold
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP, K>(), stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, K>() : 0), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -760,16 +770,17 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a); break;
   }
   }
 }
 
 template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
+  const bool cap = grid >= FSDP_CAP_MIN_TILES;
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, step_lds<OP, K>(), stream>>>(a); break;
+  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, K>() : 0), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -780,7 +791,7 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, step_lds<OP, 0>(), stream>>>(a); break;
+    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a); break;
   }
 }
 
@@ -871,9 +882,10 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
 
 void launch_multi(const MultiArgs& a, hipStream_t stream) {
   const unsigned grid = grid_for(a.tiles);
+  const size_t lds = grid >= FSDP_CAP_MIN_TILES ? lds_for_cap(FSDP_MULTI_WG_PER_CU) : 0;
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_multi<K><<<grid, kStepThreads, 0, stream>>>(a); break;
+  case K: k_step_multi<K><<<grid, kStepThreads, lds, stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
