@@ -314,6 +314,31 @@ __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, in
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
 }
 
+// The grouped fold of reduce_rows_general with compile-time counts: NG rows in
+// groups of GRP (GRP == NG: one group, i.e. the flat fold with bf16 partials),
+// all NG row loads issued before the first add. Same operations in the same
+// order as reduce_rows_general.
+template <int NG, int GRP, bool BACC>
+__device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, float gs, int64_t i,
+                                                    float (&acc)[4]) {
+  static_assert(NG % GRP == 0, "whole groups");
+  u32x2 q[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) q[k] = ldh<u32x2, kGradNt>(g[k] + i);
+#pragma unroll
+  for (int b = 0; b < NG; b += GRP) {
+    float part[4];
+    unpack(q[b], part);
+#pragma unroll
+    for (int k = 1; k < GRP; ++k) add_row<BACC>(q[b + k], part);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[e] = b == 0 ? part[e] : (BACC ? round_bf16(acc[e] + part[e]) : acc[e] + part[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = acc[e] * gs;
+}
+
 // Scalar form of the general fold of the rows at element i.
 __device__ __forceinline__ float reduce_element(const uint16_t* const* g, int ng, int group,
                                                 bool bacc, float gs, int64_t i) {
@@ -413,7 +438,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
 // Lane t of a tile owns elements [tile + kSV*t, tile + kSV*t + kSV), so every
 // load and store instruction of a wavefront covers one contiguous range; the
 // last partial group falls back to scalars.
-template <Op OP, int NG, bool EMIT>
+template <Op OP, int NG, bool EMIT, int GRP = 0, bool BACC = false>
 __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * kStepTile;
@@ -434,6 +459,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
             reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, i, g);
           else
             reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+        } else if constexpr (GRP > 0) {
+          reduce_rows_grouped<NG, GRP, BACC>(a.g, a.s.gs, i, g);
         } else {
           reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
         }
@@ -755,7 +782,18 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
     k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);   // general fold
+    // grouped folds: the common shapes with compile-time counts, the rest general
+    const size_t lds = cap ? step_lds<OP, 1>() : 0;
+    if (!a.bf16acc && a.n_grads == 16 && a.group == 8)
+      k_step_vec<OP, 16, EMIT, 8, false><<<grid, kStepThreads, lds, stream>>>(a);
+    else if (!a.bf16acc && a.n_grads == 8 && a.group == 4)
+      k_step_vec<OP, 8, EMIT, 4, false><<<grid, kStepThreads, lds, stream>>>(a);
+    else if (a.bf16acc && a.n_grads == 16 && a.group == 16)
+      k_step_vec<OP, 16, EMIT, 16, true><<<grid, kStepThreads, lds, stream>>>(a);
+    else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
+      k_step_vec<OP, 8, EMIT, 8, true><<<grid, kStepThreads, lds, stream>>>(a);
+    else
+      k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
