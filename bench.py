@@ -581,7 +581,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
     """Prints the traffic summary (markdown + JSON block) from two rocprofv3 --pmc runs."""
     import datagen.workloads as W
 
-    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true>" % F)
+    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % F)
     is_fused = lambda r: bool(fused.search(r.get("Kernel_Name", "")))
     # the calibration copy is by far the largest 4-byte copy the bench launches
     is_copy = lambda r: "k_segcopy<0>" in r.get("Kernel_Name", "")
