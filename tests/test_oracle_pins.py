@@ -344,6 +344,49 @@ def test_bf16acc_reduce_closed_forms():
     assert np.array_equal(got, ref)
 
 
+def _bf16acc_closed_form_3(a, b, c, gs):
+    """Three rows with bf16 partials, by torch's bf16 cast (a library routine):
+    bf16(fp32(bf16(fp32(a + b)) + c)) * fp32(gs), each fp32 add one rounding of
+    the exact sum."""
+    w = [O.bf16_widen(x).astype(np.float64) for x in (a, b, c)]
+    to_bf16 = lambda f32: torch.from_numpy(f32).to(torch.bfloat16).float().numpy()
+    s1 = to_bf16((w[0] + w[1]).astype(np.float32))
+    s2 = to_bf16((s1.astype(np.float64) + w[2]).astype(np.float32))
+    return (s2 * np.float32(gs)).astype(np.float32)
+
+
+def _bf16acc_inputs(n=1 << 14):
+    return [rng_bf16(131, n, 1e-3, k) for k in range(3)]
+
+
+def test_bf16acc_reduce_three_rows_closed_form():
+    a, b, c = _bf16acc_inputs()
+    L = O.unit_layout([(a.size,)], 1, 0)
+    got = O.reduce_shard_bf16acc([a, b, c], L, grad_scale=1.0 / 3)
+    assert np.array_equal(got, _bf16acc_closed_form_3(a, b, c, 1.0 / 3))
+
+
+def _mutant_round_once_at_end(rows, L, grad_scale):
+    s32 = O.reduce_shard(rows, L, grad_scale=1.0)
+    return O.bf16_widen(O.bf16_round_nearest_even(s32)) * np.float32(grad_scale)
+
+
+def _mutant_scale_before_rounding(rows, L, grad_scale):
+    acc = O.bf16_widen(rows[0][:L.shard_valid])
+    for r in rows[1:-1]:
+        acc = O.bf16_widen(O.bf16_round_nearest_even(acc + O.bf16_widen(r[:L.shard_valid])))
+    last = (acc + O.bf16_widen(rows[-1][:L.shard_valid])) * np.float32(grad_scale)
+    return O.bf16_widen(O.bf16_round_nearest_even(last))
+
+
+@pytest.mark.parametrize("mutant", [_mutant_round_once_at_end, _mutant_scale_before_rounding])
+def test_bf16acc_pin_has_teeth(mutant):
+    """Plausible mistakes in the bf16-partials fold fail the three-row closed form."""
+    a, b, c = _bf16acc_inputs()
+    L = O.unit_layout([(a.size,)], 1, 0)
+    assert not np.array_equal(mutant([a, b, c], L, 1.0 / 3), _bf16acc_closed_form_3(a, b, c, 1.0 / 3))
+
+
 def test_bf16acc_reduce_within_bf16_summation_bound():
     n_el, n = 1 << 14, 8
     gs = [datagen.bf16_bits_host(datagen.seed_for(3, 1), k, np.arange(n_el), 1e-3,
@@ -386,6 +429,62 @@ def test_hybrid_reduce_two_by_two_closed_form():
     assert np.array_equal(got, want)
     flat = O.reduce_shard(rows, O.unit_layout([(2 * n,)], 2, 0), grad_scale=1.0)
     assert not np.array_equal(got, flat)                    # the two trees round differently
+
+
+def _hybrid_closed_form_3x2(rows, n, gs=1.0):
+    """R = 3 groups of F = 2 (replica-major rows): ((p0 + p1) + p2) * fp32(gs) with
+    each pair sum p_rho one rounding of the exact pair sum, folded in group order."""
+    x = [O.bf16_widen(r[:n]).astype(np.float64) for r in rows]
+    p = [(x[2 * j] + x[2 * j + 1]).astype(np.float32) for j in range(3)]
+    acc = (p[0].astype(np.float64) + p[1]).astype(np.float32)
+    acc = (acc.astype(np.float64) + p[2]).astype(np.float32)
+    return (acc * np.float32(gs)).astype(np.float32)
+
+
+def _hybrid_inputs_3x2(n=1 << 13):
+    rows = [rng_bf16(121, n, 1e-3, k) for k in range(6)]
+    rows[1][:256] = rng_bf16(122, 256, 1e-9, 0)            # rounding inside a pair
+    rows[4][256:512] = rng_bf16(123, 256, 1e2, 0)          # a large group sum: order matters
+    return [np.concatenate([r, r]) for r in rows], n
+
+
+def test_hybrid_reduce_three_groups_closed_form():
+    rows, n = _hybrid_inputs_3x2()
+    L = O.unit_layout([(2 * n,)], 2, 0)
+    got = O.reduce_shard_hybrid(rows, L, 3, grad_scale=1.0 / 6)
+    assert np.array_equal(got, _hybrid_closed_form_3x2(rows, n, 1.0 / 6))
+
+
+def _mutant_strided_groups(rows, L, R, grad_scale):
+    F = len(rows) // R
+    return O.reduce_shard_hybrid([rows[(k % R) * F + k // R] for k in range(len(rows))], L, R,
+                                 grad_scale=grad_scale)
+
+
+def _mutant_reversed_group_order(rows, L, R, grad_scale):
+    F = len(rows) // R
+    order = [rho * F + k for rho in reversed(range(R)) for k in range(F)]
+    return O.reduce_shard_hybrid([rows[i] for i in order], L, R, grad_scale=grad_scale)
+
+
+def _mutant_scale_per_group(rows, L, R, grad_scale):
+    F = len(rows) // R
+    parts = [O.reduce_shard(rows[rho * F:(rho + 1) * F], L, grad_scale=grad_scale)
+             for rho in range(R)]
+    acc = parts[0]
+    for q in parts[1:]:
+        acc = acc + q
+    return acc
+
+
+@pytest.mark.parametrize("mutant", [_mutant_strided_groups, _mutant_reversed_group_order,
+                                    _mutant_scale_per_group])
+def test_hybrid_pin_has_teeth(mutant):
+    """Plausible mistakes in the two-level fold fail the three-group closed form."""
+    rows, n = _hybrid_inputs_3x2()
+    L = O.unit_layout([(2 * n,)], 2, 0)
+    want = _hybrid_closed_form_3x2(rows, n, 1.0 / 6)      # the default scale for 6 rows
+    assert not np.array_equal(mutant(rows, L, 3, 1.0 / 6), want)
 
 
 def test_hybrid_reduce_within_summation_bound():
