@@ -637,7 +637,42 @@ def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
     print("```json\n" + json.dumps(rec, indent=1) + "\n```")
 
 
+def trace_gaps(trace_csv: str, units: int, steps: int, warmup: int):
+    """Per-step span, kernel time and launch gaps of a whole-model sequence, from a
+    rocprofv3 kernel trace of `bench.py --workload full7b|full70b` (one launch per
+    unit per step; the library's step kernels only). Prints a markdown table."""
+    import csv
+    import statistics
+
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "k_step" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if len(rows) != units * (steps + warmup):
+        raise SystemExit(f"expected {units * (steps + warmup)} step launches, found {len(rows)}")
+    print("| step | first start → last end (ms) | sum of kernel durations (ms) | idle share | "
+          "median gap between launches (us) | largest gap (us) |")
+    print("|---|---|---|---|---|---|")
+    spans, busys = [], []
+    for s in range(warmup, warmup + steps):
+        rr = rows[s * units:(s + 1) * units]
+        st = [int(r["Start_Timestamp"]) for r in rr]
+        en = [int(r["End_Timestamp"]) for r in rr]
+        busy = sum(e - b for b, e in zip(st, en))
+        span = en[-1] - st[0]
+        gaps = [st[i + 1] - en[i] for i in range(len(rr) - 1)] or [0]
+        spans.append(span)
+        busys.append(busy)
+        print(f"| {s - warmup + 1} | {span / 1e6:.3f} | {busy / 1e6:.3f} | "
+              f"{max(0.0, 100 * (1 - busy / span)):.2f}% | {statistics.median(gaps) / 1e3:.1f} | "
+              f"{max(gaps) / 1e3:.1f} |")
+    span, busy = sum(spans) / len(spans), sum(busys) / len(busys)
+    print(f"\nmean over the timed steps: span {span / 1e6:.3f} ms, kernels {busy / 1e6:.3f} ms, "
+          f"idle {max(0.0, 100 * (1 - busy / span)):.2f}%")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-gaps":
+        trace_gaps(sys.argv[2], *(int(x) for x in sys.argv[3:6]))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         pmc_summary(sys.argv[2], sys.argv[3])
         return
