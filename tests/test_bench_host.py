@@ -93,3 +93,25 @@ def test_cpu_worker_reports_its_rate():
     rec = json.loads(r.stdout.strip().splitlines()[-1])
     assert rec["elements"] >= 2 * 2048 and rec["elements"] % 2048 == 0
     assert rec["seconds"] > 0
+
+
+def test_trace_gaps_reads_spans_and_gaps(tmp_path, capsys):
+    """Two units per step, one warm-up step: spans, kernel sums and gaps from a
+    synthetic rocprofv3 kernel trace (other kernels ignored)."""
+    hdr = '"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+    rows = []
+    t = 1000
+    for step in range(3):
+        for u in range(2):
+            rows.append(f'"KERNEL_DISPATCH","void k_step_vec<x>(StepArgs)",{t},{t + 4000}\n')
+            t += 4000 + (500 if u == 0 else 0)        # a 0.5 us gap inside each step
+        rows.append(f'"KERNEL_DISPATCH","torch_fill",{t},{t + 100}\n')
+        t += 1000
+    path = tmp_path / "trace.csv"
+    path.write_text(hdr + "".join(rows))
+    bench.trace_gaps(str(path), 2, 2, 1)
+    out = capsys.readouterr().out
+    assert "| 1 | 0.009 | 0.008 | 5.88% | 0.5 | 0.5 |" in out
+    assert "span 0.009 ms, kernels 0.008 ms" in out
+    with pytest.raises(SystemExit):
+        bench.trace_gaps(str(path), 2, 5, 1)
