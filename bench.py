@@ -686,6 +686,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--F", type=int, default=8)
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="blk7: bracket every N-th timed step with timing events")
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
@@ -787,28 +789,34 @@ def main():
         gather(i)
     torch.cuda.synchronize()
 
-    # Two timing events per step: `mid[i]` between the fused kernel and the
-    # gather, `edge[i + 1]` after the gather (which is also where step i + 1's
-    # fused kernel starts). Each event costs the stream a few microseconds, so
-    # no more are recorded than needed to time every launch.
+    # Timing events: each one recorded on the stream costs a step a few
+    # microseconds, so only every `event_every`-th step is bracketed (start,
+    # between the fused kernel and the gather, end); the kernel durations and
+    # their spread come from those steps, the step rate from the wall clock
+    # over all K steps.
     K = args.steps
-    edge = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    N = max(1, args.event_every)
+    sampled = [i for i in range(K) if i % N == 0]
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    edge[0].record(stream)
     for i in range(K):
+        e = ev.get(i)
+        if e:
+            e[0].record(stream)
         fused(W0 + i)
-        mid[i].record(stream)
+        if e:
+            e[1].record(stream)
         gather(W0 + i)
-        edge[i + 1].record(stream)
+        if e:
+            e[2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fused_ms = [edge[i].elapsed_time(mid[i]) for i in range(K)]
-    gather_ms = [mid[i].elapsed_time(edge[i + 1]) for i in range(K)]
-    step_ev_ms = [edge[i].elapsed_time(edge[i + 1]) for i in range(K)]
-    fused_avg = sum(fused_ms) / K
-    gather_avg = sum(gather_ms) / K
+    fused_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
+    gather_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in sampled]
+    step_ev_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in sampled]
+    fused_avg = sum(fused_ms) / len(fused_ms)
+    gather_avg = sum(gather_ms) / len(gather_ms)
     ms_per_step = elapsed * 1e3 / K
 
     # ---- every row of the path on its own (same rotation) -----------------
@@ -897,6 +905,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": fused_bytes,
             "avg_launch_us": fused_avg * 1e3,
+            "launches_timed": len(fused_ms),
+            "event_every": N,
         },
         "fused_us": fused_avg * 1e3,
         "fused_us_min": min(fused_ms) * 1e3,
