@@ -121,6 +121,26 @@ def test_bf16_rne_matches_torch_cast():
     assert np.all((ref[nan] & 0x7F80) == 0x7F80)     # torch also returns a NaN there
 
 
+def test_bf16_rne_matches_torch_cast_on_every_fp32_pattern():
+    """All 2^32 fp32 bit patterns: the oracle's rounding equals torch's CPU cast
+    on every non-NaN input, and both give a NaN for every NaN input."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+
+    import bf16_sweep
+
+    chunk = 1 << 25
+    starts = list(range(0, 1 << 32, chunk))
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        res = list(ex.map(bf16_sweep.check_range, starts, [chunk] * len(starts)))
+    bad = sum(r[0] for r in res)
+    firsts = [hex(r[1]) for r in res if r[1] is not None][:3]
+    assert bad == 0, f"{bad} patterns differ, first {firsts}"
+    assert sum(r[2] for r in res) == 0
+
+
 def test_bf16_rne_ties_and_overflow_closed_forms():
     halfway_past_max = np.array([0x7F7F8000], dtype=np.uint32).view(np.float32)[0]
     f = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, np.finfo(np.float32).max, -0.0,

@@ -179,6 +179,33 @@ def test_tiny_cast_unflatten_bit_exact(src):
         assert_bits(to_np(o).reshape(s), wnt, f"tensor {s}")
 
 
+def test_fp32_to_bf16_cast_on_every_fp32_pattern():
+    """The library's fp32 -> bf16 rounding (fsdp_cast_unflatten with fp32 shards,
+    the same to_bf16 as the bf16 emission) on all 2^32 fp32 bit patterns, against
+    torch's CPU cast, which the oracle's rounding equals on every pattern (the CPU
+    pins). NaN inputs must give NaN (payloads are not pinned)."""
+    chunk = 1 << 28
+    u = fsdp.Unit([(chunk,)], 1, 0)
+    out = torch.empty(chunk, dtype=torch.bfloat16, device=DEV)
+    bad, first = 0, None
+    for start in range(0, 1 << 32, chunk):
+        src = torch.arange(start, start + chunk, dtype=torch.int64, device=DEV).to(torch.int32)
+        src = src.view(torch.float32)
+        fsdp.cast_unflatten(u, [src], [out])
+        got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        x = src.cpu()
+        del src
+        want = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = torch.isnan(x).numpy()
+        got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        mism = ((got != want) & ~nan) | (nan & ~got_nan)
+        n = int(np.count_nonzero(mism))
+        if n and first is None:
+            first = hex(start + int(np.flatnonzero(mism)[0]))
+        bad += n
+    assert bad == 0, f"{bad} patterns round differently; first input bits {first}"
+
+
 def test_round_trip_flatten_then_unflatten_is_identity():
     shapes = W.shapes(W.TINY) + [(7,), (3, 5)]
     for F in (1, 3, 4, 7, 64):
