@@ -707,7 +707,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on one GPU; --gpus {args.gpus} is not "
-              "supported (the cross-GPU exchange steps are not part of this build)",
+              "supported (the cross-GPU exchange steps on either side of the shard step are not implemented here)",
               file=sys.stderr)
         sys.exit(2)
 

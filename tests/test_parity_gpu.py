@@ -1,6 +1,6 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
-Bars (fixed by the benchmark spec of the problem):
+Bars (the stated tolerances for this path's numerics):
 * flatten, pad, unflatten, indexing and bf16 copies: bit-exact;
 * fp32 master, exp_avg, exp_avg_sq and the fp32 reduced gradient: relative
   error <= 1e-6 element-wise (the design target is bit equality; the tests
