@@ -707,8 +707,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on one GPU; --gpus {args.gpus} is not "
-              "supported (the cross-GPU exchange steps on either side of the shard step are not implemented here)",
-              file=sys.stderr)
+              "supported (the cross-GPU exchange steps on either side of the shard step are "
+              "not implemented here)", file=sys.stderr)
         sys.exit(2)
 
     device = device_record() if args.workload == "blk7" else None
