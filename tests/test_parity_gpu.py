@@ -473,6 +473,52 @@ def test_blk7_sharding_factor_sweep_with_outliers_sampled(F, sweep_grads):
 
 
 # ---------------------------------------------------------------------------
+# hyper-parameters, step numbers and optimizer state other than the defaults
+# ---------------------------------------------------------------------------
+
+HP_CASES = [
+    # lr, beta1, beta2, eps, weight_decay, grad_scale, step
+    (3e-4, 0.8, 0.95, 1e-6, 0.1, 0.3, 1),
+    (1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 12345),
+    (1e-5, 0.0, 0.5, 1e-12, 0.5, 0.125, 7),
+    (2e-2, 0.99, 0.9999, 1e-8, 0.01, 1.0 / 3, 1 << 20),
+]
+
+
+@pytest.mark.parametrize("case", HP_CASES)
+@pytest.mark.parametrize("fused", [True, False])
+def test_other_hyperparameters_and_steps_bit_equal(case, fused):
+    """Fused and unfused steps from a non-zero optimizer state (m ~ N, v ~ |N|),
+    at a given step number, against the oracle, bit for bit."""
+    lr, b1, b2, eps, wd, gs, step = case
+    shapes, F, rank = [(1000, 7), (33,)], 4, 1
+    L = O.unit_layout(shapes, F, rank)
+    n = L.shard_valid
+    rng = np.random.default_rng(step)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+    rows = [datagen.bf16_bits_host(datagen.seed_for(11, 1, 1), k, np.arange(L.U), 1e-3)
+            for k in range(F)]
+    u = fsdp.Unit(shapes, F, rank)
+    dp, dm, dv = (torch.from_numpy(x.copy()).to(DEV) for x in (p, m, v))
+    dw = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    dg = [torch.from_numpy(r.view(np.int16)).to(DEV).view(torch.bfloat16) for r in rows]
+    hp = fsdp.AdamWHparams(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd)
+    if fused:
+        fsdp.reduce_adamw_shard(u, dg, dp, dm, dv, dw, hp, step, grad_scale=gs)
+    else:
+        g32 = torch.empty(u.S, dtype=torch.float32, device=DEV)
+        fsdp.reduce_shard(u, dg, g32, grad_scale=gs)
+        fsdp.adamw_shard(u, g32, dp, dm, dv, dw, hp, step)
+    torch.cuda.synchronize()
+    ohp = O.AdamW(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd)
+    want = O.reduce_adamw_shard(rows, L, p, m, v, ohp, step, grad_scale=gs, emit_bf16=True)
+    for got, exp, name in zip((dp, dm, dv, dw), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"{name} bits")
+
+
+# ---------------------------------------------------------------------------
 # design target: bit equality (stricter than the stated tolerances)
 # ---------------------------------------------------------------------------
 
