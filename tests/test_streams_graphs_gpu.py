@@ -125,3 +125,51 @@ def test_graph_captured_step_replays_like_eager():
             assert_bits(_bits(a), _bits(b), f"replay {rep}")
         scratch.normal_()                  # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_captured_capped_launches_replay_like_eager():
+    """Launches long enough to run with the occupancy cap (at least 8192 workgroups:
+    one 9M-element unit through the single-unit fused kernel, and 30 units of 300K
+    through the batched kernel) captured into a graph: every replay equals eager."""
+    big = Case([(4096, 2200)], 1, 0, config=15)             # 8800 tiles
+    mids = [Case([(600, 500)], 1, 0, config=16 + j) for j in range(30)]   # 30 x 293 tiles
+    cases = [big] + mids
+    units = [fsdp.Unit(c.shapes, c.F, c.rank) for c in cases]
+    grads = [c.device_grads(1) for c in cases]
+    start = [_state(c)[1:4] for c in cases]
+    torch.cuda.synchronize()
+
+    def state_copy():
+        return [tuple(x.clone() for x in s) + (torch.empty(u.S, dtype=torch.bfloat16, device=DEV),)
+                for s, u in zip(start, units)]
+
+    def step(st):
+        u0, (p, m, v, w) = units[0], st[0]
+        fsdp.reduce_adamw_shard(u0, grads[0], p, m, v, w, HPD, 3)
+        fsdp.reduce_adamw_units([(u, g) + tuple(s) for u, g, s in zip(units[1:], grads[1:], st[1:])],
+                                HPD, 3)
+
+    eager_st = state_copy()
+    eager = []
+    for _ in range(3):
+        step(eager_st)
+        torch.cuda.synchronize()
+        eager.append([to_np(x).copy() for s in eager_st for x in s])
+    graph_st = state_copy()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        graph.capture_begin()
+        step(graph_st)
+        graph.capture_end()
+    torch.cuda.synchronize()
+    scratch = torch.empty(1 << 20, device=DEV)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [to_np(x).copy() for s in graph_st for x in s]
+        for a, b in zip(got, eager[rep]):
+            assert_bits(_bits(a), _bits(b), f"replay {rep}")
+        scratch.normal_()
+        torch.cuda.synchronize()
