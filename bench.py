@@ -669,7 +669,34 @@ def trace_gaps(trace_csv: str, units: int, steps: int, warmup: int):
           f"idle {max(0.0, 100 * (1 - busy / span)):.2f}%")
 
 
+def trace_steps(trace_csv: str, warmup: int, steps: int, F: int = 8):
+    """Durations of the timed steps' launches in a rocprofv3 kernel trace of the
+    default (blk7) bench: a step is a fused launch followed by a gather launch;
+    the first `warmup` steps are skipped, the next `steps` are the timed ones.
+    Prints one JSON line with avg/median/p10/p90/min in us per kernel."""
+    import csv
+
+    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % F)
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    lib = [r for r in rows if "k_step" in r["Kernel_Name"] or "k_segcopy" in r["Kernel_Name"]]
+    pairs = []
+    for a, b in zip(lib, lib[1:]):
+        if fused.search(a["Kernel_Name"]) and "k_segcopy<1>" in b["Kernel_Name"]:
+            pairs.append((a, b))
+    if len(pairs) < warmup + steps:
+        raise SystemExit(f"found {len(pairs)} fused+gather steps, expected {warmup + steps}")
+    timed = pairs[warmup:warmup + steps]
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6   # ms
+    print(json.dumps({"steps": len(timed),
+                      "fused_us": spread([dur(a) for a, _ in timed]),
+                      "gather_us": spread([dur(b) for _, b in timed])}))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-steps":
+        trace_steps(sys.argv[2], int(sys.argv[3]), int(sys.argv[4]))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--trace-gaps":
         trace_gaps(sys.argv[2], *(int(x) for x in sys.argv[3:6]))
         return
