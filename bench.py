@@ -739,6 +739,11 @@ def main():
         sys.exit(2)
 
     device = device_record() if args.workload == "blk7" else None
+    if args.workload in ("full7b", "full70b"):
+        # the whole-model states are 30-180 GB: torch's expandable segments map
+        # them in large pieces, which made the 70B step's time steadier across
+        # runs (an explicit setting in the environment is kept)
+        os.environ.setdefault("PYTORCH_HIP_ALLOC_CONF", "expandable_segments:True")
 
     import torch
 
