@@ -6,9 +6,12 @@ Bars (the stated tolerances for this path's numerics):
   error <= 1e-6 element-wise (the design target is bit equality; the tests
   report the bit-equal fraction);
 * emitted bf16 parameters: <= 1 bf16 ulp.
-Small units are compared on every element; full-size units (the 7B block at
-F=8, the F sweep) on sampled indices, in the same launch configuration the
-bench uses.
+Small units are compared on every element. The 7B block at F=8 is compared on
+every element of every rank for one step, and on sampled indices over two
+steps; the F sweep on sampled indices of every rank; all in the launch
+configuration the bench uses. Also here: the tensor-count limit, other
+hyper-parameters and step numbers, and the fp32 -> bf16 rounding over all 2^32
+fp32 patterns.
 """
 
 import gc
