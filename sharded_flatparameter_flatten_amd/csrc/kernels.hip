@@ -89,7 +89,13 @@
 #define FSDP_MULTI_WG_PER_CU 3    // the batched many-unit fused kernel
 #endif
 #ifndef FSDP_CAP_MIN_TILES
-#define FSDP_CAP_MIN_TILES 8192
+#define FSDP_CAP_MIN_TILES 8192    // in 256-thread workgroups (2^23 elements)
+#endif
+// Single-unit step launches of at least 2^FSDP_HALF_TILE_MIN_LOG2 elements use
+// 128-thread workgroups (512-element tiles), with the workgroup cap doubled so
+// that a CU holds the same number of waves.
+#ifndef FSDP_HALF_TILE_MIN_LOG2
+#define FSDP_HALF_TILE_MIN_LOG2 25
 #endif
 
 using fsdp::fail;
@@ -441,8 +447,9 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
 template <Op OP, int NG, bool EMIT, int GRP = 0, bool BACC = false>
 __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
-  const int64_t stride = int64_t(gridDim.x) * kStepTile;
-  for (int64_t t0 = int64_t(blockIdx.x) * kStepTile; t0 < n; t0 += stride) {
+  const int64_t tile = int64_t(blockDim.x) * kSV;          // 128 or 256 threads per workgroup
+  const int64_t stride = int64_t(gridDim.x) * tile;
+  for (int64_t t0 = int64_t(blockIdx.x) * tile; t0 < n; t0 += stride) {
     // t0, this tile's first element, is workgroup-uniform (the store descriptors
     // are built from it in scalar registers)
     const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
           reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
         }
       }
-      const int64_t tl = n - t0 < kStepTile ? n - t0 : int64_t(kStepTile);
+      const int64_t tl = n - t0 < tile ? n - t0 : tile;
       if constexpr (OP == Op::Reduce) {
         out_f32(a.out, t0, tl, i, g);
       } else {
@@ -768,6 +775,20 @@ static_assert(cap_exact(FSDP_REDUCE_WG_PER_CU) && cap_exact(FSDP_ADAMW_WG_PER_CU
 // The fused kernels that walk a run-time row count in dependent chunks (other
 // counts, hybrid groups, bf16 partials) need every wave and stay uncapped, as
 // does the reduce-only kernel.
+static_assert(cap_exact(2 * FSDP_ADAMW_WG_PER_CU) && cap_exact(2 * FSDP_FUSED_WG_PER_CU) &&
+                  cap_exact(2 * FSDP_REDUCE_WG_PER_CU),
+              "doubled workgroup cap (half tiles) not representable");
+// The reservation for a launch of `threads`-thread workgroups: with half-size
+// workgroups the cap doubles, keeping the same waves per CU.
+template <Op OP, int NG>
+size_t step_lds_for(int threads, bool cap) {
+  if (!cap) return 0;
+  const int wg = OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
+               : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
+               : NG > 0          ? FSDP_FUSED_WG_PER_CU
+                                 : 0;
+  return lds_for_cap(wg * (kStepThreads / threads));
+}
 template <Op OP, int NG>
 constexpr size_t step_lds() {
   return lds_for_cap(OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
@@ -777,27 +798,28 @@ constexpr size_t step_lds() {
 }
 
 template <Op OP, bool EMIT>
-void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
-  const bool cap = grid >= FSDP_CAP_MIN_TILES;
+void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, hipStream_t stream) {
+  // the cap applies to launches of at least FSDP_CAP_MIN_TILES full-size tiles
+  const bool cap = int64_t(grid) * threads >= int64_t(FSDP_CAP_MIN_TILES) * kStepThreads;
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
     // grouped folds: the common shapes with compile-time counts, the rest general
-    const size_t lds = cap ? step_lds<OP, 1>() : 0;
+    const size_t lds = step_lds_for<OP, 1>(threads, cap);
     if (!a.bf16acc && a.n_grads == 16 && a.group == 8)
-      k_step_vec<OP, 16, EMIT, 8, false><<<grid, kStepThreads, lds, stream>>>(a);
+      k_step_vec<OP, 16, EMIT, 8, false><<<grid, threads, lds, stream>>>(a);
     else if (!a.bf16acc && a.n_grads == 8 && a.group == 4)
-      k_step_vec<OP, 8, EMIT, 4, false><<<grid, kStepThreads, lds, stream>>>(a);
+      k_step_vec<OP, 8, EMIT, 4, false><<<grid, threads, lds, stream>>>(a);
     else if (a.bf16acc && a.n_grads == 16 && a.group == 16)
-      k_step_vec<OP, 16, EMIT, 16, true><<<grid, kStepThreads, lds, stream>>>(a);
+      k_step_vec<OP, 16, EMIT, 16, true><<<grid, threads, lds, stream>>>(a);
     else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
-      k_step_vec<OP, 8, EMIT, 8, true><<<grid, kStepThreads, lds, stream>>>(a);
+      k_step_vec<OP, 8, EMIT, 8, true><<<grid, threads, lds, stream>>>(a);
     else
-      k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a);
+      k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a);
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, K>() : 0), stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, threads, step_lds_for<OP, K>(threads, cap), stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -808,11 +830,10 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a); break;
   }
   }
 }
-
 template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
   const bool cap = grid >= FSDP_CAP_MIN_TILES;
@@ -839,9 +860,12 @@ template <Op OP>
 fsdp_status launch_step(const StepArgs& a, Path path, hipStream_t stream, const char* what) {
   if (a.n <= 0) return FSDP_OK;
   if (path == Path::Vector) {
-    const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);
-    if (a.w) launch_vec_ng<OP, true>(a, grid, stream);
-    else launch_vec_ng<OP, false>(a, grid, stream);
+    const int threads =
+        a.n >= (int64_t(1) << FSDP_HALF_TILE_MIN_LOG2) ? kStepThreads / 2 : kStepThreads;
+    const int64_t tile = int64_t(threads) * kSV;
+    const unsigned grid = grid_for((a.n + tile - 1) / tile);
+    if (a.w) launch_vec_ng<OP, true>(a, grid, threads, stream);
+    else launch_vec_ng<OP, false>(a, grid, threads, stream);
   } else if (path == Path::Shifted) {
     if constexpr (OP != Op::AdamW) {
       const unsigned grid = grid_for((a.n + 4 * kStepThreads - 1) / (4 * kStepThreads));
