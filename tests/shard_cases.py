@@ -9,6 +9,8 @@ a sampled index's whole multi-step trajectory can be recomputed on its own.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -160,15 +162,22 @@ def gather(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
     return to_np(t[torch.from_numpy(idx).to(t.device)])
 
 
+# FSDP_STRICT_BITS=1 turns the tolerance checks below into bit equality (the
+# design target), to confirm that every compared element is bit-equal.
+STRICT = os.environ.get("FSDP_STRICT_BITS", "0") == "1"
+
+
 def assert_rel(got, want, tol=1e-6, what=""):
     """Element-wise relative error <= tol (exact where the expected value is 0)."""
+    if STRICT:
+        tol = 0.0
     got = np.asarray(got, dtype=np.float32)
     want = np.asarray(want, dtype=np.float32)
     assert got.shape == want.shape, what
     same = got.view(np.uint32) == want.view(np.uint32)
     g64, w64 = got.astype(np.float64), want.astype(np.float64)
     err = np.abs(g64 - w64)
-    ok = same | (err <= tol * np.abs(w64))
+    ok = same if STRICT else same | (err <= tol * np.abs(w64))
     if not ok.all():
         bad = np.flatnonzero(~ok)[:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} elements beyond rel {tol}; first "
@@ -182,6 +191,8 @@ def bf16_ordinal(bits):
 
 
 def assert_bf16_ulp(got, want, ulps=1, what=""):
+    if STRICT:
+        ulps = 0
     got = np.asarray(got, dtype=np.uint16)
     want = np.asarray(want, dtype=np.uint16)
     d = np.abs(bf16_ordinal(got) - bf16_ordinal(want))
