@@ -21,6 +21,11 @@
 //    back while the next kernel ran and slowed it; the streaming stores
 //    finish inside the kernel that issues them, and the 7B-block step
 //    (fused + gather) went from ~318 us to ~307 us;
+//  * occupancy, also chosen by measurement: long launches of the fused kernels
+//    with a compile-time row count and of the stand-alone AdamW kernel run
+//    with 12 waves per CU (3 workgroups of 256 threads, held down by unused
+//    dynamic LDS) rather than 32; single-unit launches of 2^25+ elements use
+//    128-thread workgroups (512-element tiles) and 6 workgroups per CU;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
