@@ -10,7 +10,14 @@ ROOT = os.path.dirname(os.path.dirname(HERE))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from sharded_flatparameter_flatten_amd import build as libbuild  # noqa: E402
+import importlib.util  # noqa: E402
+
+# the library's build script, loaded by its path (importing it through the
+# package would load the library itself)
+_spec = importlib.util.spec_from_file_location(
+    "fsdpshard_build", os.path.join(ROOT, "sharded_flatparameter_flatten_amd", "build.py"))
+libbuild = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(libbuild)
 
 PROBE = "libfp32probe.so"
 
