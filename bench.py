@@ -15,9 +15,13 @@ One step = the whole per-unit hot path of the rank:
 (The indexer and the flatten/pad of the master weights run once at init.)
 
 Prints one JSON line. value = shard params/s (shard_valid per step / step
-time); roofline = the fused kernel's algorithmic bytes / its average duration
-from HIP events on its stream; cpu_baseline = the CPU oracle on a bounded
-sample of the same workload.
+time, the wall clock over the --steps headline steps); roofline = the fused
+kernel's algorithmic bytes / its average duration over a sample of at least
+64 further in-step launches, each bracketed by HIP events on its stream (the
+same sample is taken on rank F-1); stream_mix_ceiling = the same loads and
+stores without the AdamW arithmetic (a reference kernel under tests/probes),
+timed the same way; cpu_baseline = the CPU oracle on a bounded sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -265,6 +269,92 @@ def rotating_rows(torch, datagen, W, unit, n_rows, n_sets, dev, seed, outlier_se
             rows.append(row)
         out.append(rows)
     return out
+
+
+def make_sets(fsdp, torch, datagen, W, units, rank, R, dev, separate=True, keep_masters=True):
+    """R independent buffer sets of the 7B-block step for `rank`: gradient rows
+    (that rank's window filled), fp32 master (flattened from per-tensor draws),
+    m, v, every rank's bf16 shard, and the 9 bf16 outputs of the gather."""
+    u = units[rank]
+    F, S = u.F, u.S
+    shapes = u.shapes
+    row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1),
+                             separate=separate)
+    sets, set_masters = [], []
+    for j in range(R):
+        masters = []
+        for i, nel in enumerate(u.numels):
+            t = torch.empty(nel, dtype=torch.float32, device=dev)
+            datagen.fill_normal_f32_(t, datagen.seed_for(1, 0), 256 * j + i, W.MASTER_SIGMA)
+            masters.append(t)
+        p = torch.empty(S, dtype=torch.float32, device=dev)
+        fsdp.flatten_pad(u, masters, p)                   # init: flatten + pad (once)
+        masters_bf16 = [t.to(torch.bfloat16) for t in masters]
+        shards = []
+        for r in range(F):                                # every rank's bf16 parameter shard
+            sh = torch.empty(S, dtype=torch.bfloat16, device=dev)
+            fsdp.flatten_pad(units[r], masters_bf16, sh)
+            shards.append(sh)
+        del masters_bf16
+        m = torch.zeros(S, dtype=torch.float32, device=dev)
+        v = torch.zeros(S, dtype=torch.float32, device=dev)
+        outs = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes]
+        sets.append((row_sets[j], p, m, v, shards, outs))
+        set_masters.append(masters if keep_masters else None)
+    return sets, set_masters
+
+
+def bracketed_steps(torch, stream, fused, gather, first, L):
+    """L steps (fused, then gather) with each kernel bracketed by HIP events on
+    `stream`; returns the fused and gather intervals in ms."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
+    torch.cuda.synchronize()
+    for i in range(L):
+        ev[i][0].record(stream)
+        fused(first + i)
+        ev[i][1].record(stream)
+        gather(first + i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    return ([e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev])
+
+
+STREAM_MIX_LIB = os.path.join(ROOT, "tests", "probes", "libstreammix.so")
+
+
+def stream_mix_leg(torch, stream, sets, u, rank, F, gather, first, L):
+    """The stream-mix reference kernel in the step loop (see stream_mix_probe.hip),
+    or None when it is not built or the workload is not 8 rows on a 4-aligned shard."""
+    import ctypes
+    n = u.shard_valid
+    if F != 8 or n % 4 or (2 * u.shard_begin) % 8 or not os.path.exists(STREAM_MIX_LIB):
+        return None
+    lib = ctypes.CDLL(STREAM_MIX_LIB)
+    lib.probe_stream_mix.restype = ctypes.c_int
+    lib.probe_stream_mix.argtypes = [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    # the library's shape for this launch: one-wave workgroups, 8 per CU
+    threads, wg_per_cu = 64, 8
+    R = len(sets)
+    rows = []
+    for grads, p, m, v, shards, outs in sets:
+        arr = (ctypes.c_void_p * 8)(*[g.data_ptr() + 2 * u.shard_begin for g in grads])
+        rows.append((arr, p.data_ptr(), m.data_ptr(), v.data_ptr(), shards[rank].data_ptr()))
+
+    def mix(i):
+        arr, p, m, v, w = rows[i % R]
+        st = lib.probe_stream_mix(arr, p, m, v, w, n, threads, wg_per_cu, stream.cuda_stream)
+        if st:
+            raise RuntimeError(f"probe_stream_mix returned {st}")
+
+    for i in range(R):
+        mix(first + i)
+        gather(first + i)
+    f, _ = bracketed_steps(torch, stream, mix, gather, first, L)
+    return {"kernel": "stream-mix reference (8 bf16 row reads, 3 fp32 reads, 3 fp32 + 1 bf16 "
+                      "writes per element; no AdamW arithmetic)",
+            "threads": threads, "wg_per_cu": wg_per_cu, "launches_timed": len(f),
+            "us": spread(f)}
 
 
 CALIB_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB)
@@ -715,6 +805,9 @@ def main():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=4,
                     help="blk7: bracket every N-th timed step with timing events")
+    ap.add_argument("--roofline-steps", type=int, default=64,
+                    help="blk7: steps of the roofline sample (every fused launch bracketed; "
+                         "at least 64)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent buffer sets visited in turn (1 = repeat one set)")
     ap.add_argument("--workload", default="blk7", choices=["blk7", "full7b", "full70b", "sweep", "state_dict", "hybrid"])
@@ -779,29 +872,8 @@ def main():
     # ---- inputs resident in HBM: R independent sets, visited in turn -------
     # (every set has its own gradient windows, optimizer state, bf16 shards and
     # outputs, so no step finds the previous step's data in a cache)
-    row_sets = rotating_rows(torch, datagen, W, u, F, R, dev, datagen.seed_for(1, 1, 1),
-                             separate=args.row_layout == "separate")
-    sets, set_masters = [], []
-    for j in range(R):
-        masters = []
-        for i, nel in enumerate(u.numels):
-            t = torch.empty(nel, dtype=torch.float32, device=dev)
-            datagen.fill_normal_f32_(t, datagen.seed_for(1, 0), 256 * j + i, W.MASTER_SIGMA)
-            masters.append(t)
-        p = torch.empty(S, dtype=torch.float32, device=dev)
-        fsdp.flatten_pad(u, masters, p)                   # init: flatten + pad (once)
-        masters_bf16 = [t.to(torch.bfloat16) for t in masters]
-        shards = []
-        for r in range(F):                                # every rank's bf16 parameter shard
-            sh = torch.empty(S, dtype=torch.bfloat16, device=dev)
-            fsdp.flatten_pad(units[r], masters_bf16, sh)
-            shards.append(sh)
-        del masters_bf16
-        m = torch.zeros(S, dtype=torch.float32, device=dev)
-        v = torch.zeros(S, dtype=torch.float32, device=dev)
-        outs = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in shapes]
-        sets.append((row_sets[j], p, m, v, shards, outs))
-        set_masters.append(masters)
+    sets, set_masters = make_sets(fsdp, torch, datagen, W, units, rank, R, dev,
+                                  separate=args.row_layout == "separate")
     hp = fsdp.AdamWHparams(**W.ADAMW)
     torch.cuda.synchronize()
 
@@ -821,11 +893,10 @@ def main():
         gather(i)
     torch.cuda.synchronize()
 
-    # Timing events: each one recorded on the stream costs a step a few
-    # microseconds, so only every `event_every`-th step is bracketed (start,
-    # between the fused kernel and the gather, end); the kernel durations and
-    # their spread come from those steps, the step rate from the wall clock
-    # over all K steps.
+    # Headline: K steps timed by the wall clock (value, ms_per_step). Timing
+    # events cost the stream a few microseconds each, so only every
+    # `event_every`-th of these steps is bracketed (start, between the fused
+    # kernel and the gather, end); timing_us reports those steps.
     K = args.steps
     N = max(1, args.event_every)
     sampled = [i for i in range(K) if i % N == 0]
@@ -847,9 +918,51 @@ def main():
     fused_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
     gather_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in sampled]
     step_ev_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in sampled]
-    fused_avg = sum(fused_ms) / len(fused_ms)
-    gather_avg = sum(gather_ms) / len(gather_ms)
     ms_per_step = elapsed * 1e3 / K
+
+    # Roofline sample: the same step loop run for `roofline_steps` more steps
+    # (at least 64, whatever --steps is) with every fused launch bracketed, so
+    # the kernel's average duration rests on that many launches.
+    Lr = max(args.roofline_steps, 64)
+    roof_f, roof_g = bracketed_steps(torch, stream, fused, gather, W0 + K, Lr)
+    fused_avg = sum(roof_f) / len(roof_f)
+    gather_avg = sum(roof_g) / len(roof_g)
+
+    # The same sample on rank F-1 (its own rotating sets: the last window of
+    # every gradient row).
+    last = None
+    if F > 1 and rank != F - 1:
+        ul = units[F - 1]
+        sets_l, _ = make_sets(fsdp, torch, datagen, W, units, F - 1, R, dev,
+                              separate=args.row_layout == "separate", keep_masters=False)
+
+        def fused_l(i):
+            grads, p, m, v, shards, outs = sets_l[i % R]
+            fsdp.reduce_adamw_shard(ul, grads, p, m, v, shards[F - 1], hp, i // R + 1,
+                                    stream=stream)
+
+        def gather_l(i):
+            grads, p, m, v, shards, outs = sets_l[i % R]
+            fsdp.cast_unflatten(ul, shards, outs, stream=stream)
+
+        for i in range(W0):
+            fused_l(i)
+            gather_l(i)
+        lf, lg = bracketed_steps(torch, stream, fused_l, gather_l, W0, Lr)
+        nl = ul.shard_valid
+        last = {"rank": F - 1, "shard_params": nl, "launches_timed": len(lf),
+                "algorithmic_bytes_per_launch": (2 * F + 26) * nl,
+                "fused_us": spread(lf), "gather_us": spread(lg),
+                "achieved": (2 * F + 26) * nl / (sum(lf) / len(lf) * 1e-3) / 1e9,
+                "frac": (2 * F + 26) * nl / (sum(lf) / len(lf) * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del sets_l
+        torch.cuda.empty_cache()
+
+    # Stream-mix ceiling: the fused kernel's loads and stores without the
+    # AdamW arithmetic (tests/probes/stream_mix_probe.hip), in the same step
+    # loop over the same sets, in the workgroup shape the library picks for
+    # this launch.
+    mix = stream_mix_leg(torch, stream, sets, u, rank, F, gather, W0, Lr)
 
     # ---- every row of the path on its own (same rotation) -----------------
     g32 = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(R)]
@@ -906,6 +1019,9 @@ def main():
     fused_bytes = (2 * F + 26) * n                # bf16 rows + fp32 p/m/v in/out + bf16 out
     gather_bytes = 4 * u.U                        # bf16 in (F*S valid) + bf16 out
     achieved = fused_bytes / (fused_avg * 1e-3) / 1e9
+    if mix is not None:
+        mix["GBps"] = fused_bytes / (mix["us"]["avg"] * 1e-6) / 1e9
+        mix["fused_us_over_ceiling_us"] = fused_avg * 1e3 / mix["us"]["avg"]
     traffic = read_traffic()
     result = {
         "metric": METRIC,
@@ -937,18 +1053,24 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": fused_bytes,
             "avg_launch_us": fused_avg * 1e3,
-            "launches_timed": len(fused_ms),
-            "event_every": N,
+            "median_launch_us": spread(roof_f)["median"],
+            "p90_launch_us": spread(roof_f)["p90"],
+            "launches_timed": len(roof_f),
+            "protocol": (f"{len(roof_f)} in-step launches after the headline loop, each "
+                         "bracketed by HIP events on the launch stream; rotating sets"),
         },
+        "roofline_rank_last": last,
+        "stream_mix_ceiling": mix,
         "fused_us": fused_avg * 1e3,
-        "fused_us_min": min(fused_ms) * 1e3,
+        "fused_us_min": min(roof_f) * 1e3,
         "gather_us": gather_avg * 1e3,
         "gather_GBps": gather_bytes / (gather_avg * 1e-3) / 1e9,
         "step_GBps": (fused_bytes + gather_bytes) / (ms_per_step * 1e-3) / 1e9,
         "unit_params_per_s": u.U / (ms_per_step * 1e-3),
         "copy_GBps": copy_gbps,
-        "timing_us": {"fused": spread(fused_ms), "gather": spread(gather_ms),
-                      "step": spread(step_ev_ms)},
+        "timing_us": {"event_every": N, "fused": spread(fused_ms), "gather": spread(gather_ms),
+                      "step": spread(step_ev_ms), "roofline_fused": spread(roof_f),
+                      "roofline_gather": spread(roof_g)},
         "rows_alone": rows,
         "warm_secondary": {"fused_us": warm_us,
                            "GBps": (2 * F + 26) * n / (warm_us * 1e-6) / 1e9,

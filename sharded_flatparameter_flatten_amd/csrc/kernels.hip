@@ -21,11 +21,13 @@
 //    back while the next kernel ran and slowed it; the streaming stores
 //    finish inside the kernel that issues them, and the 7B-block step
 //    (fused + gather) went from ~318 us to ~307 us;
-//  * occupancy, also chosen by measurement: long launches of the fused kernels
-//    with a compile-time row count and of the stand-alone AdamW kernel run
-//    with 12 waves per CU (3 workgroups of 256 threads, held down by unused
-//    dynamic LDS) rather than 32; single-unit launches of 2^25+ elements use
-//    128-thread workgroups (512-element tiles) and 6 workgroups per CU;
+//  * occupancy, also chosen by measurement (step_shape below): long fused
+//    launches with a compile-time fold of 4+ gradient rows run one-wave
+//    workgroups (256-element tiles), 8 per CU; other long launches of the
+//    fused kernels with a compile-time row count and of the stand-alone AdamW
+//    kernel run 12 waves per CU (3 workgroups of 256 threads, or 6 of 128
+//    threads at 2^25+ elements); the per-CU counts are held down by unused
+//    dynamic LDS sized from the device's LDS per CU;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
@@ -42,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -77,10 +80,10 @@
 #define FSDP_COPY_STORE_CPOL 18
 #endif
 
-// Resident step workgroups per CU (0: no cap). The cap is imposed with unused
-// dynamic LDS, a CU holding 160 KiB of it, and only on launches of at least
-// FSDP_CAP_MIN_TILES workgroups: a shorter launch has fewer tiles than a few
-// rounds of a full machine and runs best with every workgroup resident.
+// Resident 256-thread step workgroups per CU (0: no cap). The cap is imposed
+// with unused dynamic LDS, and only on launches of at least 2^FSDP_CAP_MIN_LOG2
+// elements: a shorter launch has fewer tiles than a few rounds of a full
+// machine and runs best with every workgroup resident.
 #ifndef FSDP_REDUCE_WG_PER_CU
 #define FSDP_REDUCE_WG_PER_CU 0
 #endif
@@ -93,14 +96,26 @@
 #ifndef FSDP_MULTI_WG_PER_CU
 #define FSDP_MULTI_WG_PER_CU 3    // the batched many-unit fused kernel
 #endif
-#ifndef FSDP_CAP_MIN_TILES
-#define FSDP_CAP_MIN_TILES 8192    // in 256-thread workgroups (2^23 elements)
+#ifndef FSDP_CAP_MIN_LOG2
+#define FSDP_CAP_MIN_LOG2 23       // launches of 2^23+ elements are capped
 #endif
 // Single-unit step launches of at least 2^FSDP_HALF_TILE_MIN_LOG2 elements use
 // 128-thread workgroups (512-element tiles), with the workgroup cap doubled so
 // that a CU holds the same number of waves.
 #ifndef FSDP_HALF_TILE_MIN_LOG2
 #define FSDP_HALF_TILE_MIN_LOG2 25
+#endif
+// Fused launches with a compile-time flat fold of at least FSDP_SMALL_WG_MIN_ROWS
+// rows on 2^FSDP_SMALL_WG_MIN_LOG2+ elements: one-wave workgroups, at most
+// FSDP_SMALL_WG_PER_CU per CU.
+#ifndef FSDP_SMALL_WG_MIN_LOG2
+#define FSDP_SMALL_WG_MIN_LOG2 24
+#endif
+#ifndef FSDP_SMALL_WG_MIN_ROWS
+#define FSDP_SMALL_WG_MIN_ROWS 4
+#endif
+#ifndef FSDP_SMALL_WG_PER_CU
+#define FSDP_SMALL_WG_PER_CU 8
 #endif
 
 using fsdp::fail;
@@ -109,6 +124,7 @@ namespace {
 
 constexpr int kThreads = FSDP_COPY_BLOCK;
 constexpr int kStepThreads = FSDP_STEP_BLOCK;
+constexpr int kSmallThreads = 64;   // one wave
 constexpr int kSV = 4;   // consecutive elements per lane in the step kernels
 constexpr int64_t kStepTile = int64_t(kStepThreads) * kSV;
 
@@ -452,7 +468,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
 template <Op OP, int NG, bool EMIT, int GRP = 0, bool BACC = false>
 __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
-  const int64_t tile = int64_t(blockDim.x) * kSV;          // 128 or 256 threads per workgroup
+  const int64_t tile = int64_t(blockDim.x) * kSV;          // 64, 128 or 256 threads per workgroup
   const int64_t stride = int64_t(gridDim.x) * tile;
   for (int64_t t0 = int64_t(blockIdx.x) * tile; t0 < n; t0 += stride) {
     // t0, this tile's first element, is workgroup-uniform (the store descriptors
@@ -762,55 +778,88 @@ fsdp_status after_launch(const char* what) {
   return FSDP_OK;
 }
 
-// The reservation is the largest 4 KiB multiple of which wg_per_cu fit in a
-// CU, so that allocation granules cannot round it up past that count.
-constexpr size_t kLdsPerCu = 160 * 1024;
-constexpr size_t lds_for_cap(int wg_per_cu) {
-  return wg_per_cu <= 0 ? 0 : (kLdsPerCu / wg_per_cu) / 4096 * 4096;
+// LDS per CU of the current device (queried once; 0 if the query fails, which
+// leaves every launch uncapped).
+int lds_per_cu() {
+  static std::atomic<int> cached{-1};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v >= 0) return v;
+  int dev = 0, bytes = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess)
+    bytes = 0;
+  cached.store(bytes, std::memory_order_relaxed);
+  return bytes;
 }
-constexpr bool cap_exact(int wg_per_cu) {
-  return wg_per_cu <= 0 || (wg_per_cu + 1) * lds_for_cap(wg_per_cu) > kLdsPerCu;
+
+// Unused dynamic LDS that caps resident workgroups at wg_per_cu per CU: the
+// largest 4 KiB multiple (else 512 B multiple) of which wg_per_cu fit in a CU
+// and wg_per_cu + 1 do not, so allocation granules cannot round it past that
+// count. 0 (no cap) when no such size exists.
+size_t lds_reservation(int wg_per_cu) {
+  const int64_t per_cu = lds_per_cu();
+  if (wg_per_cu <= 0 || per_cu <= 0) return 0;
+  for (int64_t granule : {int64_t(4096), int64_t(512)}) {
+    const int64_t r = per_cu / wg_per_cu / granule * granule;
+    if (r > 0 && (wg_per_cu + 1) * r > per_cu) return size_t(r);
+  }
+  return 0;
 }
-static_assert(cap_exact(FSDP_REDUCE_WG_PER_CU) && cap_exact(FSDP_ADAMW_WG_PER_CU) &&
-                  cap_exact(FSDP_FUSED_WG_PER_CU) && cap_exact(FSDP_MULTI_WG_PER_CU),
-              "workgroup cap not representable by a 4 KiB LDS reservation");
-// LDS bytes a step workgroup reserves. With the streaming stores, the
-// stand-alone AdamW kernel and the fused kernels with a compile-time row count
-// (all row loads in flight at once) are fastest with three workgroups per CU.
-// The fused kernels that walk a run-time row count in dependent chunks (other
-// counts, hybrid groups, bf16 partials) need every wave and stay uncapped, as
-// does the reduce-only kernel.
-static_assert(cap_exact(2 * FSDP_ADAMW_WG_PER_CU) && cap_exact(2 * FSDP_FUSED_WG_PER_CU) &&
-                  cap_exact(2 * FSDP_REDUCE_WG_PER_CU),
-              "doubled workgroup cap (half tiles) not representable");
-// The reservation for a launch of `threads`-thread workgroups: with half-size
-// workgroups the cap doubles, keeping the same waves per CU.
-template <Op OP, int NG>
-size_t step_lds_for(int threads, bool cap) {
-  if (!cap) return 0;
-  const int wg = OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
-               : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
-               : NG > 0          ? FSDP_FUSED_WG_PER_CU
-                                 : 0;
-  return lds_for_cap(wg * (kStepThreads / threads));
+
+// Occupancy plan of a vector-path step launch: workgroup size and resident
+// workgroups per CU (0: as many as fit). Chosen by measurement on MI355X
+// (rotating buffer sets, several boxes and allocations):
+//  * launches under 2^23 elements run every workgroup they have at once;
+//  * the fused step with a compile-time fold of at least FSDP_SMALL_WG_MIN_ROWS
+//    rows, on 2^FSDP_SMALL_WG_MIN_LOG2 elements or more, runs one-wave
+//    workgroups (256-element tiles), 8 per CU: each lane then has 8n+48 bytes
+//    of loads in flight, and 8 waves per CU keep enough bytes in flight while
+//    the small tiles keep the write streams of one CU short and the tail of
+//    the launch short;
+//  * other launches of 2^FSDP_HALF_TILE_MIN_LOG2 elements or more run
+//    128-thread workgroups, with the per-CU count of their 256-thread form
+//    doubled (same waves per CU);
+//  * the stand-alone AdamW kernel and the fused kernels with a compile-time
+//    fold run at most 3 workgroups of 256 threads per CU (12 waves); the
+//    fused kernels that walk a run-time row count in dependent chunks, and
+//    the reduce-only kernel, are never capped.
+struct Shape {
+  int threads;
+  int wg_per_cu;
+};
+
+bool compile_time_fold(const StepArgs& a) {
+  if (a.group < a.n_grads || a.bf16acc)
+    return (!a.bf16acc && a.n_grads == 16 && a.group == 8) ||
+           (!a.bf16acc && a.n_grads == 8 && a.group == 4) ||
+           (a.bf16acc && a.n_grads == 16 && a.group == 16) ||
+           (a.bf16acc && a.n_grads == 8 && a.group == 8);
+  return (a.n_grads >= 1 && a.n_grads <= 8) || a.n_grads == 16;
 }
-template <Op OP, int NG>
-constexpr size_t step_lds() {
-  return lds_for_cap(OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
-                     : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
-                     : NG > 0          ? FSDP_FUSED_WG_PER_CU
-                                       : 0);
+
+template <Op OP>
+Shape step_shape(const StepArgs& a) {
+  const bool fixed = OP != Op::AdamW && compile_time_fold(a);
+  const bool flat = a.group == a.n_grads && !a.bf16acc;
+  const int base = OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
+                 : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
+                 : fixed           ? FSDP_FUSED_WG_PER_CU
+                                   : 0;
+  if (a.n < (int64_t(1) << FSDP_CAP_MIN_LOG2)) return Shape{kStepThreads, 0};
+  if (OP == Op::Fused && fixed && flat && a.n_grads >= FSDP_SMALL_WG_MIN_ROWS &&
+      a.n >= (int64_t(1) << FSDP_SMALL_WG_MIN_LOG2))
+    return Shape{kSmallThreads, FSDP_SMALL_WG_PER_CU};
+  if (a.n >= (int64_t(1) << FSDP_HALF_TILE_MIN_LOG2)) return Shape{kStepThreads / 2, 2 * base};
+  return Shape{kStepThreads, base};
 }
 
 template <Op OP, bool EMIT>
-void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, hipStream_t stream) {
-  // the cap applies to launches of at least FSDP_CAP_MIN_TILES full-size tiles
-  const bool cap = int64_t(grid) * threads >= int64_t(FSDP_CAP_MIN_TILES) * kStepThreads;
+void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, size_t lds, hipStream_t stream) {
   if constexpr (OP == Op::AdamW) {
-    k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a);
+    k_step_vec<OP, 0, EMIT><<<grid, threads, lds, stream>>>(a);
   } else if (a.group < a.n_grads || a.bf16acc) {
     // grouped folds: the common shapes with compile-time counts, the rest general
-    const size_t lds = step_lds_for<OP, 1>(threads, cap);
     if (!a.bf16acc && a.n_grads == 16 && a.group == 8)
       k_step_vec<OP, 16, EMIT, 8, false><<<grid, threads, lds, stream>>>(a);
     else if (!a.bf16acc && a.n_grads == 8 && a.group == 4)
@@ -820,11 +869,11 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, hipStream_t st
     else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
       k_step_vec<OP, 8, EMIT, 8, true><<<grid, threads, lds, stream>>>(a);
     else
-      k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a);
+      k_step_vec<OP, 0, EMIT><<<grid, threads, lds, stream>>>(a);
   } else {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_vec<OP, K, EMIT><<<grid, threads, step_lds_for<OP, K>(threads, cap), stream>>>(a); break;
+  case K: k_step_vec<OP, K, EMIT><<<grid, threads, lds, stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -835,16 +884,19 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, hipStream_t st
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_vec<OP, 0, EMIT><<<grid, threads, step_lds_for<OP, 0>(threads, cap), stream>>>(a); break;
+    default: k_step_vec<OP, 0, EMIT><<<grid, threads, lds, stream>>>(a); break;
   }
   }
 }
 template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
-  const bool cap = grid >= FSDP_CAP_MIN_TILES;
+  // 256-thread workgroups, capped like the vector path's 256-thread form
+  const bool cap = a.n >= (int64_t(1) << FSDP_CAP_MIN_LOG2);
+  const int base = OP == Op::Reduce ? FSDP_REDUCE_WG_PER_CU : FSDP_FUSED_WG_PER_CU;
+  const size_t lds = cap ? lds_reservation(base) : 0;
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, K>() : 0), stream>>>(a); break;
+  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, lds, stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -855,7 +907,7 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, (cap ? step_lds<OP, 0>() : 0), stream>>>(a); break;
+    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, (cap && OP == Op::Reduce ? lds : 0), stream>>>(a); break;
   }
 }
 
@@ -865,12 +917,12 @@ template <Op OP>
 fsdp_status launch_step(const StepArgs& a, Path path, hipStream_t stream, const char* what) {
   if (a.n <= 0) return FSDP_OK;
   if (path == Path::Vector) {
-    const int threads =
-        a.n >= (int64_t(1) << FSDP_HALF_TILE_MIN_LOG2) ? kStepThreads / 2 : kStepThreads;
-    const int64_t tile = int64_t(threads) * kSV;
+    const Shape sh = step_shape<OP>(a);
+    const int64_t tile = int64_t(sh.threads) * kSV;
     const unsigned grid = grid_for((a.n + tile - 1) / tile);
-    if (a.w) launch_vec_ng<OP, true>(a, grid, threads, stream);
-    else launch_vec_ng<OP, false>(a, grid, threads, stream);
+    const size_t lds = lds_reservation(sh.wg_per_cu);
+    if (a.w) launch_vec_ng<OP, true>(a, grid, sh.threads, lds, stream);
+    else launch_vec_ng<OP, false>(a, grid, sh.threads, lds, stream);
   } else if (path == Path::Shifted) {
     if constexpr (OP != Op::AdamW) {
       const unsigned grid = grid_for((a.n + 4 * kStepThreads - 1) / (4 * kStepThreads));
@@ -949,7 +1001,8 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
 
 void launch_multi(const MultiArgs& a, hipStream_t stream) {
   const unsigned grid = grid_for(a.tiles);
-  const size_t lds = grid >= FSDP_CAP_MIN_TILES ? lds_for_cap(FSDP_MULTI_WG_PER_CU) : 0;
+  const size_t lds =
+      a.tiles * kStepTile >= (int64_t(1) << FSDP_CAP_MIN_LOG2) ? lds_reservation(FSDP_MULTI_WG_PER_CU) : 0;
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
   case K: k_step_multi<K><<<grid, kStepThreads, lds, stream>>>(a); break;

@@ -20,19 +20,29 @@ libbuild = importlib.util.module_from_spec(_spec)
 _spec.loader.exec_module(libbuild)
 
 PROBE = "libfp32probe.so"
+STREAM_MIX = "libstreammix.so"
 
 
 def path() -> str:
     return os.path.join(HERE, PROBE)
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(HERE, "fp32_ops_probe.hip")
-    tmp = path() + ".tmp"
+def stream_mix_path() -> str:
+    return os.path.join(HERE, STREAM_MIX)
+
+
+def _build_one(src_name: str, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
     libbuild._run([libbuild.HIPCC, "-x", "hip", *libbuild.DEVICE, *libbuild.COMMON, "-shared",
-                   src, "-o", tmp], verbose)
-    os.replace(tmp, path())
-    return path()
+                   os.path.join(HERE, src_name), "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds both probes; returns the fp32 probe's path."""
+    _build_one("stream_mix_probe.hip", stream_mix_path(), verbose)
+    return _build_one("fp32_ops_probe.hip", path(), verbose)
 
 
 if __name__ == "__main__":
