@@ -375,6 +375,21 @@ def copy_reference(fsdp, torch, dev, stream, reps=10):
     return 2 * 4 * CALIB_ELEMS * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
+def torch_copy_reference(torch, dev, reps=2):
+    """torch's own device copy of 1 GiB of fp32 (a known-size transfer that
+    shares no code with the library); returns GB/s."""
+    src = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2 * 4 * CALIB_ELEMS * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
 def model_sequence(args):
     """Whole-model rank shard: one step = fused reduce+AdamW+bf16 emit for every unit in order."""
     import torch
@@ -656,73 +671,100 @@ def _counter_rows(path):
     return rows
 
 
-def _per_dispatch(rows, match, counter):
-    """Counter value (summed over its instances) per dispatch of kernels matching `match`."""
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum",
+                 "TCC_EA0_RDREQ_DRAM_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum")
+READ_REQUEST_BYTES = 128     # gfx950 L2 -> memory read request (see pmc_summary)
+
+
+def _dispatch_counters(rows, match):
+    """{dispatch id: {counter: value summed over instances}} for kernels matching `match`."""
     acc = {}
     for r in rows:
-        if r.get("Counter_Name") != counter or not match(r):
+        if not match(r.get("Kernel_Name", "")):
             continue
         key = r.get("Dispatch_Id") or r.get("Correlation_Id")
-        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
-    return list(acc.values())
+        d = acc.setdefault(key, {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return acc
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, F: int = 8):
-    """Prints the traffic summary (markdown + JSON block) from two rocprofv3 --pmc runs."""
+def _request_bytes(rd, wr):
+    """HBM bytes of one dispatch from the raw L2 <-> memory request counts:
+    reads are 128-byte requests (TCC_EA0_RDREQ, none of them 32-byte), writes
+    64-byte (TCC_EA0_WRREQ_64B) or 32-byte (the rest of TCC_EA0_WRREQ)."""
+    r32 = rd.get("TCC_EA0_RDREQ_32B_sum", 0.0)
+    read = READ_REQUEST_BYTES * (rd["TCC_EA0_RDREQ_sum"] - r32) + 32 * r32
+    w64 = wr["TCC_EA0_WRREQ_64B_sum"]
+    write = 64 * w64 + 32 * (wr["TCC_EA0_WRREQ_sum"] - w64)
+    return read, write
+
+
+def pmc_summary(read_dir: str, write_dir: str, F: int = 8):
+    """Prints the traffic summary (markdown + JSON block) from two rocprofv3
+    --pmc runs of `bench.py --quick`: one with READ_COUNTERS, one with
+    WRITE_COUNTERS.
+
+    On gfx950 an L2 -> memory read request moves a 128-byte line. The derived
+    FETCH_SIZE metric counts a request as 128 bytes only through TCC_BUBBLE,
+    which stays 0 for these kernels, so it reports half the bytes read. The
+    128-byte size is checked here on two 1 GiB copies of known size: the HIP
+    runtime's own device copy (torch's copy_) and the library's fp32 copy;
+    both must come out within 0.1% of 2^30 bytes read and written."""
     import datagen.workloads as W
 
     fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % F)
-    is_fused = lambda r: bool(fused.search(r.get("Kernel_Name", "")))
-    # the calibration copy is by far the largest 4-byte copy the bench launches
-    is_copy = lambda r: "k_segcopy<0>" in r.get("Kernel_Name", "")
-    largest = lambda xs: [x for x in xs if x >= 0.5 * max(xs)] if xs else xs
-    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
-    f_fused = _per_dispatch(fr, is_fused, "FETCH_SIZE")
-    w_fused = _per_dispatch(wr, is_fused, "WRITE_SIZE")
-    f_copy = largest(_per_dispatch(fr, is_copy, "FETCH_SIZE"))
-    w_copy = largest(_per_dispatch(wr, is_copy, "WRITE_SIZE"))
-    if not (f_fused and w_fused and f_copy and w_copy):
-        raise SystemExit("missing dispatches: fused %d/%d copy %d/%d" % (
-            len(f_fused), len(w_fused), len(f_copy), len(w_copy)))
+    rr, wr = _counter_rows(read_dir), _counter_rows(write_dir)
+    kinds = {
+        "fused": lambda n: bool(fused.search(n)),
+        "gather": lambda n: "k_segcopy<1>" in n,
+        "library_copy": lambda n: "k_segcopy<0>" in n,
+        "runtime_copy": lambda n: "copyBuffer" in n,
+    }
     avg = lambda x: sum(x) / len(x)
-    cal_bytes = 4 * CALIB_ELEMS
-    kf = cal_bytes / (avg(f_copy) * 1024)          # known bytes / counted bytes
-    kw = cal_bytes / (avg(w_copy) * 1024)
-    rd = avg(f_fused) * 1024 * kf
-    wt = avg(w_fused) * 1024 * kw
+    per = {}
+    for kind, match in kinds.items():
+        dr, dw = _dispatch_counters(rr, match), _dispatch_counters(wr, match)
+        pairs = [_request_bytes(dr[k], dw_k) for k, dw_k in
+                 zip(sorted(dr, key=int), [dw[k] for k in sorted(dw, key=int)])]
+        if not pairs:
+            raise SystemExit(f"no {kind} dispatches in the counter runs")
+        tot = [a + b for a, b in pairs]
+        # the gathers and the 1 GiB copies are the largest launches of their kernel
+        keep = [i for i, t in enumerate(tot) if t >= 0.5 * max(tot)]
+        per[kind] = {
+            "dispatches": len(keep),
+            "read_bytes": avg([pairs[i][0] for i in keep]),
+            "write_bytes": avg([pairs[i][1] for i in keep]),
+            "raw": {c: avg([dr[k][c] for k in [sorted(dr, key=int)[i] for i in keep]])
+                    for c in READ_COUNTERS},
+            "raw_write": {c: avg([dw[k][c] for k in [sorted(dw, key=int)[i] for i in keep]])
+                          for c in WRITE_COUNTERS},
+        }
+    gib = float(1 << 30)
+    for kind in ("runtime_copy", "library_copy"):
+        c = per[kind]
+        c["read_over_known"] = c["read_bytes"] / gib
+        c["write_over_known"] = c["write_bytes"] / gib
+        if not (abs(c["read_over_known"] - 1) < 1e-3 and abs(c["write_over_known"] - 1) < 1e-3):
+            raise SystemExit(f"{kind}: counted bytes do not match its 1 GiB: {c}")
     U = sum(math.prod(sh) for sh in W.shapes(W.BLK7))
     valid = min(-(-U // F), U)                    # rank 0's shard: ceil(U / F) elements
     alg_r, alg_w = (2 * F + 12) * valid, 14 * valid
-    # the gathers: the bf16 copies that move a whole unit (the init-time
-    # flattens of single shards are an F-th of that)
-    is_gather = lambda r: "k_segcopy<1>" in r.get("Kernel_Name", "")
-    f_g = largest(_per_dispatch(fr, is_gather, "FETCH_SIZE"))
-    w_g = largest(_per_dispatch(wr, is_gather, "WRITE_SIZE"))
-    gather = None
-    if f_g and w_g:
-        g_rd, g_wt = avg(f_g) * 1024 * kf, avg(w_g) * 1024 * kw
-        gather = {
-            "kernel": "k_segcopy<1> (fsdp_cast_unflatten, %d bf16 shards -> 9 tensors)" % F,
-            "dispatches": [len(f_g), len(w_g)],
-            "fetch_kib_per_dispatch": avg(f_g), "write_kib_per_dispatch": avg(w_g),
-            "hbm_read_bytes_per_launch": g_rd, "hbm_write_bytes_per_launch": g_wt,
-            "algorithmic_read_bytes": 2 * U, "algorithmic_write_bytes": 2 * U,
-            "traffic_over_algorithmic": (g_rd + g_wt) / (4 * U),
-        }
+    f, g = per["fused"], per["gather"]
     rec = {
         "kernel": "k_step_vec<Fused, %d, emit> (fused reduce+AdamW+bf16 emit)" % F,
         "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, valid),
         "kernels_hip_sha256_16": kernel_source_hash(),
-        "fused_dispatches": [len(f_fused), len(w_fused)],
-        "fetch_kib_per_dispatch": avg(f_fused), "write_kib_per_dispatch": avg(w_fused),
-        "calibration": "k_segcopy<0>, 1 GiB fp32 read + 1 GiB written",
-        "calib_fetch_kib": avg(f_copy), "calib_write_kib": avg(w_copy),
-        "fetch_scale": kf, "write_scale": kw,
-        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wt,
-        "hbm_bytes_per_launch": rd + wt,
+        "read_request_bytes": READ_REQUEST_BYTES,
+        "fused": f, "hbm_read_bytes_per_launch": f["read_bytes"],
+        "hbm_write_bytes_per_launch": f["write_bytes"],
+        "hbm_bytes_per_launch": f["read_bytes"] + f["write_bytes"],
         "algorithmic_read_bytes": alg_r, "algorithmic_write_bytes": alg_w,
-        "traffic_over_algorithmic": (rd + wt) / (alg_r + alg_w),
-        "gather": gather,
+        "traffic_over_algorithmic": (f["read_bytes"] + f["write_bytes"]) / (alg_r + alg_w),
+        "gather": dict(g, algorithmic_bytes=4 * U,
+                       traffic_over_algorithmic=(g["read_bytes"] + g["write_bytes"]) / (4 * U)),
+        "known_size_checks": {k: per[k] for k in ("runtime_copy", "library_copy")},
     }
     print("```json\n" + json.dumps(rec, indent=1) + "\n```")
 
@@ -821,6 +863,9 @@ def main():
     ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],
                     help="blk7: one allocation per gradient row, or all rows' windows in one arena")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true",
+                    help="blk7: only the headline steps and the two 1 GiB reference copies "
+                         "(for profiler runs)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     args = ap.parse_args()
@@ -832,11 +877,6 @@ def main():
         sys.exit(2)
 
     device = device_record() if args.workload == "blk7" else None
-    if args.workload in ("full7b", "full70b"):
-        # the whole-model states are 30-180 GB: torch's expandable segments map
-        # them in large pieces, which made the 70B step's time steadier across
-        # runs (an explicit setting in the environment is kept)
-        os.environ.setdefault("PYTORCH_HIP_ALLOC_CONF", "expandable_segments:True")
 
     import torch
 
@@ -919,6 +959,15 @@ def main():
     gather_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in sampled]
     step_ev_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in sampled]
     ms_per_step = elapsed * 1e3 / K
+
+    if args.quick:
+        # profiler runs: the headline steps, then the two known-size copies
+        # (the library's 1 GiB fp32 copy and torch's copy of the same size)
+        copy_reference(fsdp, torch, dev, stream, reps=2)
+        torch_copy_reference(torch, dev, reps=2)
+        print(json.dumps({"workload": "blk7", "quick": True, "steps": K,
+                          "ms_per_step": elapsed * 1e3 / K}), flush=True)
+        return
 
     # Roofline sample: the same step loop run for `roofline_steps` more steps
     # (at least 64, whatever --steps is) with every fused launch bracketed, so

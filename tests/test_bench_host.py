@@ -115,3 +115,50 @@ def test_trace_gaps_reads_spans_and_gaps(tmp_path, capsys):
     assert "span 0.009 ms, kernels 0.008 ms" in out
     with pytest.raises(SystemExit):
         bench.trace_gaps(str(path), 2, 5, 1)
+
+
+def _counter_csv(path, dispatches):
+    """A rocprofv3 counter_collection.csv holding `dispatches` = [(kernel, {counter: value})]."""
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n']
+    for i, (kernel, counters) in enumerate(dispatches):
+        for c, v in counters.items():
+            # two instances per counter, summed by the reader
+            lines.append(f'"{i + 1}","{kernel}","{c}","{v / 2}"\n')
+            lines.append(f'"{i + 1}","{kernel}","{c}","{v / 2}"\n')
+    path.mkdir()
+    (path / "run_counter_collection.csv").write_text("".join(lines))
+
+
+def test_traffic_summary_from_raw_request_counts(tmp_path, capsys):
+    """Bytes from 128-byte read and 64-byte write requests; the two 1 GiB copies of known
+    size gate the result, and a copy whose counts do not match its size stops it."""
+    U, S = 202383360, 25297920
+    fused = "void (anonymous namespace)::k_step_vec<((anonymous namespace)::Op)2, 8, true, 0, false>(x)"
+    gather = "void (anonymous namespace)::k_segcopy<1>((anonymous namespace)::SegArgs)"
+    lcopy = "void (anonymous namespace)::k_segcopy<0>((anonymous namespace)::SegArgs)"
+    rcopy = "__amd_rocclr_copyBuffer"
+    gib = 1 << 30
+
+    def rd(nbytes):
+        return {"TCC_EA0_RDREQ_sum": nbytes / 128, "TCC_EA0_RDREQ_32B_sum": 0.0,
+                "TCC_BUBBLE_sum": 0.0, "TCC_EA0_RDREQ_DRAM_sum": nbytes / 128}
+
+    def wr(nbytes):
+        return {"TCC_EA0_WRREQ_sum": nbytes / 64, "TCC_EA0_WRREQ_64B_sum": nbytes / 64,
+                "TCC_EA0_WRREQ_DRAM_sum": nbytes / 64}
+
+    seq = [(fused, 28 * S, 14 * S), (gather, 2 * U, 2 * U), (gather, 2 * S, 2 * S),
+           (fused, 28 * S + 128, 14 * S), (lcopy, gib, gib), (rcopy, gib, gib)]
+    _counter_csv(tmp_path / "rd", [(k, rd(r)) for k, r, _ in seq])
+    _counter_csv(tmp_path / "wr", [(k, wr(w)) for k, _, w in seq])
+    bench.pmc_summary(str(tmp_path / "rd"), str(tmp_path / "wr"))
+    rec = json.loads(capsys.readouterr().out.split("```json")[1].split("```")[0])
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(42 * S + 64)
+    assert rec["traffic_over_algorithmic"] == pytest.approx(1 + 64 / (42 * S))
+    assert rec["gather"]["dispatches"] == 1          # the init-size copy is left out
+    assert rec["gather"]["traffic_over_algorithmic"] == pytest.approx(1.0)
+    bad = [(k, r if k != rcopy else gib // 2, w) for k, r, w in seq]
+    _counter_csv(tmp_path / "rd2", [(k, rd(r)) for k, r, _ in bad])
+    _counter_csv(tmp_path / "wr2", [(k, wr(w)) for k, _, w in bad])
+    with pytest.raises(SystemExit):
+        bench.pmc_summary(str(tmp_path / "rd2"), str(tmp_path / "wr2"))
