@@ -26,9 +26,21 @@
  * - Execution: every device entry point only enqueues work on `stream`
  *   (NULL = the null stream) and returns; there is no implicit
  *   synchronisation, allocation or host<->device copy. Arguments are checked
- *   before anything is enqueued, so a call that returns an error has
- *   enqueued nothing. A fault inside a kernel surfaces at the caller's next
- *   synchronisation, not as a return code.
+ *   and every launch is planned before anything is enqueued, so a call that
+ *   fails a check has enqueued nothing. Before its first launch a call also
+ *   checks the calling thread's HIP error state (hipPeekAtLastError): if an
+ *   error from earlier work is pending it returns FSDP_ERR_HIP, enqueues
+ *   nothing and leaves that error in place. FSDP_ERR_HIP after that means
+ *   the runtime refused a launch: a call of one launch has then enqueued
+ *   nothing; a call that needs several (fsdp_reduce_adamw_units, and
+ *   fsdp_flatten_pad / fsdp_unflatten beyond 64 copy segments) keeps the
+ *   launches before the refused one enqueued. A fault inside a kernel
+ *   surfaces at the caller's next synchronisation, not as a return code.
+ * - Empty windows: when a step call's shard_valid is 0 (a rank whose window
+ *   holds only pad), it checks its counts and hyper-parameters and returns
+ *   FSDP_OK without touching its buffer arguments, which may then be NULL;
+ *   the same holds for fsdp_flatten_pad with len 0, and fsdp_unflatten reads
+ *   no shard that holds only pad and writes no tensor of 0 elements.
  * - Aliasing: the byte ranges a call writes must not overlap each other or
  *   the ranges it reads (FSDP_ERR_ALIAS); master/exp_avg/exp_avg_sq are read
  *   and written in place by design.
@@ -229,9 +241,10 @@ typedef struct {
  * large operations rather than many small ones. Aligned entries with
  * n_grads <= 8 and fewer than 2^22 shard elements are stepped together, one
  * kernel launch per up to 30 units; larger or unaligned entries get one
- * launch each. All entries are validated (including overlaps
- * between different units' buffers) before anything is enqueued.
- * n_units == 0 is a no-op. */
+ * launch each, in the order given. All entries are validated (including
+ * overlaps between different units' buffers) and every launch is planned
+ * before anything is enqueued; entries whose shard_valid is 0 are skipped (their
+ * buffers may be NULL). n_units == 0 is a no-op. */
 fsdp_status fsdp_reduce_adamw_units(int32_t n_units, const fsdp_unit_step* steps,
                                     int32_t n_grads, const fsdp_adamw_hparams* hp,
                                     hipStream_t stream);

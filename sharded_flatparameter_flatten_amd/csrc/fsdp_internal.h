@@ -34,20 +34,25 @@ fsdp_status fail(fsdp_status st, const char* fmt, ...)
     __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// A byte range [lo, hi) a call reads or writes, named for error messages.
+// A byte range [lo, hi) a call reads or writes. Its name for error messages
+// is built only when a conflict is reported: `label` (a string literal),
+// `index` within a pointer array (or -1), and the unit of a multi-unit call
+// (or -1).
 struct ByteRange {
   uintptr_t lo;
   uintptr_t hi;
   bool write;
-  std::string name;
+  const char* label;
+  int32_t index;
+  int32_t unit;
 };
 
 ByteRange range_of(const void* p, int64_t elems, int64_t elem_bytes, bool write,
-                   const std::string& name);
+                   const char* label, int32_t index = -1, int32_t unit = -1);
 
 // FSDP_OK when no written range overlaps any other range; reads may overlap
-// each other.
-fsdp_status check_alias(std::vector<ByteRange> ranges);
+// each other. Sorts `ranges` in place.
+fsdp_status check_alias(std::vector<ByteRange>& ranges);
 
 // Host fp32 scalars of one AdamW step, each rounded once from double.
 struct AdamScalars {

@@ -787,8 +787,10 @@ int lds_per_cu() {
   int dev = 0, bytes = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-          hipSuccess)
+          hipSuccess) {
     bytes = 0;
+    (void)hipGetLastError();   // the caller checked that no earlier error was pending
+  }
   cached.store(bytes, std::memory_order_relaxed);
   return bytes;
 }
@@ -942,19 +944,38 @@ struct Piece {
   int64_t len;
 };
 
-// Splits each piece into an unaligned scalar head and an aligned vector body
-// (each side on one lane's access width) when some head
-// length h < EPL aligns both sides; otherwise the whole piece is scalar. Then
-// launches the segments in batches of kMaxSeg.
-fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_t stream,
-                          const char* what) {
+// Per-thread scratch vectors of the host side, reused from call to call so
+// that a call's validation and planning allocate nothing once a thread has
+// made a few calls.
+template <typename T, int TAG>
+std::vector<T>& scratch() {
+  thread_local std::vector<T> v;
+  v.clear();
+  return v;
+}
+
+// A HIP error left pending by earlier work on this thread would come back as
+// this call's launch failure: refuse to enqueue anything instead, and leave
+// the error where it is for its owner (nothing is cleared).
+fsdp_status check_no_pending_error(const char* what) {
+  const hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess)
+    return fail(FSDP_ERR_HIP, "%s: a HIP error from earlier work is pending (%s); nothing was "
+                "enqueued", what, hipGetErrorString(e));
+  return FSDP_OK;
+}
+
+// Plans the segment-copy launches of `pieces`: each piece splits into an
+// unaligned scalar head and an aligned vector body (each side on one lane's
+// access width) when some head length h < EPL aligns both sides, otherwise
+// the whole piece is scalar; the segments then go in batches of kMaxSeg.
+void plan_pieces(const std::vector<Piece>& pieces, int kind, std::vector<SegArgs>* batches) {
   const int64_t ss = (kind == 1 || kind == 3) ? 2 : 4;   // source element bytes
   const int64_t ds = (kind == 0 || kind == 3) ? 4 : 2;   // destination element bytes
   const int64_t epl = copy_epl(kind);
   const uintptr_t smask = uintptr_t(epl * ss - 1);
   const uintptr_t dmask = uintptr_t(epl * ds - 1);
-  std::vector<Seg> segs;
-  segs.reserve(pieces.size() * 2);
+  std::vector<Seg>& segs = scratch<Seg, 0>();
   for (const Piece& pc : pieces) {
     if (pc.len <= 0) continue;
     const uintptr_t s0 = reinterpret_cast<uintptr_t>(pc.src);
@@ -977,7 +998,9 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     segs.push_back(Seg{vs, vd, pc.len - head, 0, vmode, 0});
   }
   for (size_t b = 0; b < segs.size(); b += kMaxSeg) {
-    SegArgs a{};
+    batches->emplace_back();
+    SegArgs& a = batches->back();
+    a = SegArgs{};
     const size_t nb = std::min<size_t>(kMaxSeg, segs.size() - b);
     int64_t tiles = 0;
     for (size_t j = 0; j < nb; ++j) {
@@ -987,7 +1010,15 @@ fsdp_status launch_pieces(const std::vector<Piece>& pieces, int kind, hipStream_
     }
     a.nseg = static_cast<int32_t>(nb);
     a.tiles = tiles;
-    const unsigned grid = grid_for(tiles);
+  }
+}
+
+// Launches planned segment-copy batches in order. If the runtime refuses
+// launch k, launches 0..k-1 stay enqueued (documented in the header).
+fsdp_status launch_batches(const std::vector<SegArgs>& batches, int kind, hipStream_t stream,
+                           const char* what) {
+  for (const SegArgs& a : batches) {
+    const unsigned grid = grid_for(a.tiles);
     switch (kind) {
       case 0: k_segcopy<0><<<grid, kThreads, 0, stream>>>(a); break;
       case 1: k_segcopy<1><<<grid, kThreads, 0, stream>>>(a); break;
@@ -1023,12 +1054,16 @@ Adam to_device(const fsdp::AdamScalars& h) {
   return Adam{h.gs, h.b1, h.omb1, h.b2, h.omb2, h.bc1, h.bc2, h.lr, h.eps, h.wd};
 }
 
-fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
-                        std::vector<fsdp::ByteRange>* ranges, StepArgs* a,
-                        const std::string& who = "") {
+fsdp_status check_n_grads(int32_t n_grads) {
   if (n_grads < 1 || n_grads > FSDP_MAX_RANKS)
     return fail(FSDP_ERR_INVALID_ARG, "n_grads must be in [1, %d] (got %d)", FSDP_MAX_RANKS,
                 n_grads);
+  return FSDP_OK;
+}
+
+// The gradient rows of a step call (only when the rank's window holds data).
+fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
+                        std::vector<fsdp::ByteRange>* ranges, StepArgs* a, int32_t unit = -1) {
   if (!grads) return fail(FSDP_ERR_INVALID_ARG, "grads array is NULL");
   for (int32_t k = 0; k < n_grads; ++k) {
     if (!grads[k]) return fail(FSDP_ERR_INVALID_ARG, "grads[%d] is NULL", k);
@@ -1036,8 +1071,7 @@ fsdp_status check_grads(const fsdp_unit* u, int32_t n_grads, const void* const* 
       return fail(FSDP_ERR_INVALID_ARG, "grads[%d] is not 2-byte aligned", k);
     const uint16_t* w = static_cast<const uint16_t*>(grads[k]) + u->begin;
     a->g[k] = w;
-    ranges->push_back(
-        fsdp::range_of(w, u->valid, 2, false, who + "grads[" + std::to_string(k) + "]"));
+    ranges->push_back(fsdp::range_of(w, u->valid, 2, false, "grads", k, unit));
   }
   a->n_grads = n_grads;
   a->group = n_grads;
@@ -1074,7 +1108,7 @@ Path step_path(const StepArgs& a, Op op) {
 
 fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float* exp_avg_sq,
                         void* w, std::vector<fsdp::ByteRange>* ranges, StepArgs* a,
-                        const std::string& who = "") {
+                        int32_t unit = -1) {
   if (fsdp_status st = check_f32(master, "master")) return st;
   if (fsdp_status st = check_f32(exp_avg, "exp_avg")) return st;
   if (fsdp_status st = check_f32(exp_avg_sq, "exp_avg_sq")) return st;
@@ -1084,10 +1118,65 @@ fsdp_status check_state(const fsdp_unit* u, float* master, float* exp_avg, float
   a->m = exp_avg;
   a->v = exp_avg_sq;
   a->w = static_cast<uint16_t*>(w);
-  ranges->push_back(fsdp::range_of(master, u->valid, 4, true, who + "master"));
-  ranges->push_back(fsdp::range_of(exp_avg, u->valid, 4, true, who + "exp_avg"));
-  ranges->push_back(fsdp::range_of(exp_avg_sq, u->valid, 4, true, who + "exp_avg_sq"));
-  if (w) ranges->push_back(fsdp::range_of(w, u->valid, 2, true, who + "param_bf16_out"));
+  ranges->push_back(fsdp::range_of(master, u->valid, 4, true, "master", -1, unit));
+  ranges->push_back(fsdp::range_of(exp_avg, u->valid, 4, true, "exp_avg", -1, unit));
+  ranges->push_back(fsdp::range_of(exp_avg_sq, u->valid, 4, true, "exp_avg_sq", -1, unit));
+  if (w) ranges->push_back(fsdp::range_of(w, u->valid, 2, true, "param_bf16_out", -1, unit));
+  return FSDP_OK;
+}
+
+// The shared body of the reduce-only entry points (flat, hybrid, bf16 partials).
+fsdp_status reduce_entry(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
+                         double grad_scale, float* out, int32_t group, int32_t bf16acc,
+                         hipStream_t stream, const char* what) {
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (fsdp_status st = check_n_grads(n_grads)) return st;
+  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
+  if (u->valid == 0) return FSDP_OK;            // a window of pad only: nothing to do
+  StepArgs a{};
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_f32(out, "out")) return st;
+  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.group = group > 0 ? group : n_grads;
+  a.bf16acc = bf16acc;
+  a.out = out;
+  a.n = u->valid;
+  a.s.gs = static_cast<float>(grad_scale);
+  if (fsdp_status st = check_no_pending_error(what)) return st;
+  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream, what);
+}
+
+// The shared body of the fused single-unit entry points.
+fsdp_status fused_entry(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
+                        float* master, float* exp_avg, float* exp_avg_sq, void* param_bf16_out,
+                        const fsdp_adamw_hparams* hp, int32_t group, int32_t bf16acc,
+                        hipStream_t stream, const char* what) {
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (fsdp_status st = check_n_grads(n_grads)) return st;
+  fsdp::AdamScalars hs;
+  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
+  if (u->valid == 0) return FSDP_OK;            // a window of pad only: nothing to do
+  StepArgs a{};
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
+  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
+  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
+    return st;
+  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
+  a.group = group > 0 ? group : n_grads;
+  a.bf16acc = bf16acc;
+  a.n = u->valid;
+  a.s = to_device(hs);
+  if (fsdp_status st = check_no_pending_error(what)) return st;
+  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream, what);
+}
+
+fsdp_status check_replicas(const fsdp_unit* u, int32_t replicas) {
+  if (fsdp_status st = fsdp::check_unit(u)) return st;
+  if (replicas < 1 || int64_t(replicas) * u->F > FSDP_MAX_RANKS)
+    return fail(FSDP_ERR_INVALID_ARG, "replicas * F must be in [1, %d] (replicas=%d, F=%d)",
+                FSDP_MAX_RANKS, replicas, u->F);
   return FSDP_OK;
 }
 
@@ -1098,18 +1187,7 @@ extern "C" {
 fsdp_status fsdp_reduce_shard(const fsdp_unit* u, int32_t n_grads, const void* const* grads,
                               double grad_scale, float* out, hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_f32(out, "out")) return st;
-  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.out = out;
-  a.n = u->valid;
-  a.s.gs = static_cast<float>(grad_scale);
-  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream, "fsdp_reduce_shard");
+  return reduce_entry(u, n_grads, grads, grad_scale, out, 0, 0, stream, "fsdp_reduce_shard");
 }
 
 fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* master,
@@ -1119,8 +1197,9 @@ fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* maste
   if (fsdp_status st = fsdp::check_unit(u)) return st;
   fsdp::AdamScalars hs;
   if (fsdp_status st = fsdp::derive_adam_scalars(hp, false, &hs)) return st;
+  if (u->valid == 0) return FSDP_OK;            // a window of pad only: nothing to do
   StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
   if (fsdp_status st = check_f32(grad, "grad")) return st;
   ranges.push_back(fsdp::range_of(grad, u->valid, 4, false, "grad"));
   if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
@@ -1129,6 +1208,7 @@ fsdp_status fsdp_adamw_shard(const fsdp_unit* u, const float* grad, float* maste
   a.grad = grad;
   a.n = u->valid;
   a.s = to_device(hs);
+  if (fsdp_status st = check_no_pending_error("fsdp_adamw_shard")) return st;
   return launch_step<Op::AdamW>(a, step_path(a, Op::AdamW), stream, "fsdp_adamw_shard");
 }
 
@@ -1137,39 +1217,16 @@ fsdp_status fsdp_reduce_adamw_shard(const fsdp_unit* u, int32_t n_grads,
                                     float* exp_avg_sq, void* param_bf16_out,
                                     const fsdp_adamw_hparams* hp, hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  fsdp::AdamScalars hs;
-  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
-    return st;
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.n = u->valid;
-  a.s = to_device(hs);
-  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
-                                "fsdp_reduce_adamw_shard");
+  return fused_entry(u, n_grads, grads, master, exp_avg, exp_avg_sq, param_bf16_out, hp, 0, 0,
+                     stream, "fsdp_reduce_adamw_shard");
 }
 
 fsdp_status fsdp_reduce_shard_bf16acc(const fsdp_unit* u, int32_t n_grads,
                                       const void* const* grads, double grad_scale, float* out,
                                       hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_f32(out, "out")) return st;
-  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.bf16acc = 1;
-  a.out = out;
-  a.n = u->valid;
-  a.s.gs = static_cast<float>(grad_scale);
-  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream,
-                                 "fsdp_reduce_shard_bf16acc");
+  return reduce_entry(u, n_grads, grads, grad_scale, out, 0, 1, stream,
+                      "fsdp_reduce_shard_bf16acc");
 }
 
 fsdp_status fsdp_reduce_adamw_shard_bf16acc(const fsdp_unit* u, int32_t n_grads,
@@ -1178,42 +1235,17 @@ fsdp_status fsdp_reduce_adamw_shard_bf16acc(const fsdp_unit* u, int32_t n_grads,
                                             void* param_bf16_out, const fsdp_adamw_hparams* hp,
                                             hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  fsdp::AdamScalars hs;
-  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, n_grads, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
-    return st;
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.bf16acc = 1;
-  a.n = u->valid;
-  a.s = to_device(hs);
-  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
-                                "fsdp_reduce_adamw_shard_bf16acc");
+  return fused_entry(u, n_grads, grads, master, exp_avg, exp_avg_sq, param_bf16_out, hp, 0, 1,
+                     stream, "fsdp_reduce_adamw_shard_bf16acc");
 }
 
 fsdp_status fsdp_reduce_shard_hybrid(const fsdp_unit* u, int32_t replicas,
                                      const void* const* grads, double grad_scale, float* out,
                                      hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  if (replicas < 1 || int64_t(replicas) * u->F > FSDP_MAX_RANKS)
-    return fail(FSDP_ERR_INVALID_ARG, "replicas * F must be in [1, %d] (replicas=%d, F=%d)",
-                FSDP_MAX_RANKS, replicas, u->F);
-  if (!std::isfinite(grad_scale)) return fail(FSDP_ERR_INVALID_ARG, "grad_scale must be finite");
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, replicas * u->F, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_f32(out, "out")) return st;
-  ranges.push_back(fsdp::range_of(out, u->valid, 4, true, "out"));
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.group = u->F;
-  a.out = out;
-  a.n = u->valid;
-  a.s.gs = static_cast<float>(grad_scale);
-  return launch_step<Op::Reduce>(a, step_path(a, Op::Reduce), stream, "fsdp_reduce_shard_hybrid");
+  if (fsdp_status st = check_replicas(u, replicas)) return st;
+  return reduce_entry(u, replicas * u->F, grads, grad_scale, out, u->F, 0, stream,
+                      "fsdp_reduce_shard_hybrid");
 }
 
 fsdp_status fsdp_reduce_adamw_shard_hybrid(const fsdp_unit* u, int32_t replicas,
@@ -1222,82 +1254,93 @@ fsdp_status fsdp_reduce_adamw_shard_hybrid(const fsdp_unit* u, int32_t replicas,
                                            void* param_bf16_out, const fsdp_adamw_hparams* hp,
                                            hipStream_t stream) {
   fsdp::clear_error();
-  if (fsdp_status st = fsdp::check_unit(u)) return st;
-  if (replicas < 1 || int64_t(replicas) * u->F > FSDP_MAX_RANKS)
-    return fail(FSDP_ERR_INVALID_ARG, "replicas * F must be in [1, %d] (replicas=%d, F=%d)",
-                FSDP_MAX_RANKS, replicas, u->F);
-  fsdp::AdamScalars hs;
-  if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
-  StepArgs a{};
-  std::vector<fsdp::ByteRange> ranges;
-  if (fsdp_status st = check_grads(u, replicas * u->F, grads, &ranges, &a)) return st;
-  if (fsdp_status st = check_state(u, master, exp_avg, exp_avg_sq, param_bf16_out, &ranges, &a))
-    return st;
-  if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  a.group = u->F;
-  a.n = u->valid;
-  a.s = to_device(hs);
-  return launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
-                                "fsdp_reduce_adamw_shard_hybrid");
+  if (fsdp_status st = check_replicas(u, replicas)) return st;
+  return fused_entry(u, replicas * u->F, grads, master, exp_avg, exp_avg_sq, param_bf16_out, hp,
+                     u->F, 0, stream, "fsdp_reduce_adamw_shard_hybrid");
 }
 
 fsdp_status fsdp_reduce_adamw_units(int32_t n_units, const fsdp_unit_step* steps, int32_t n_grads,
                                     const fsdp_adamw_hparams* hp, hipStream_t stream) {
   fsdp::clear_error();
+  const char* what = "fsdp_reduce_adamw_units";
   if (n_units < 0) return fail(FSDP_ERR_INVALID_ARG, "n_units must be >= 0 (got %d)", n_units);
   if (n_units == 0) return FSDP_OK;
   if (!steps) return fail(FSDP_ERR_INVALID_ARG, "steps array is NULL");
+  if (fsdp_status st = check_n_grads(n_grads)) return st;
   fsdp::AdamScalars hs;
   if (fsdp_status st = fsdp::derive_adam_scalars(hp, true, &hs)) return st;
-  std::vector<StepArgs> args(static_cast<size_t>(n_units));
-  std::vector<fsdp::ByteRange> ranges;
+  std::vector<StepArgs>& args = scratch<StepArgs, 0>();
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
   for (int32_t i = 0; i < n_units; ++i) {
     const fsdp_unit_step& st_i = steps[i];
-    const std::string who = "unit " + std::to_string(i) + " ";
     if (!st_i.unit) return fail(FSDP_ERR_INVALID_ARG, "steps[%d].unit is NULL", i);
-    StepArgs& a = args[static_cast<size_t>(i)];
+    if (st_i.unit->valid == 0) continue;        // a window of pad only: nothing to do
+    args.emplace_back();
+    StepArgs& a = args.back();
     a = StepArgs{};
-    if (fsdp_status st = check_grads(st_i.unit, n_grads, st_i.grads, &ranges, &a, who)) return st;
+    if (fsdp_status st = check_grads(st_i.unit, n_grads, st_i.grads, &ranges, &a, i)) {
+      const std::string msg = fsdp_last_error();
+      return fail(st, "steps[%d]: %s", i, msg.c_str());
+    }
     if (fsdp_status st = check_state(st_i.unit, st_i.master, st_i.exp_avg, st_i.exp_avg_sq,
-                                     st_i.param_bf16_out, &ranges, &a, who))
-      return st;
+                                     st_i.param_bf16_out, &ranges, &a, i)) {
+      const std::string msg = fsdp_last_error();
+      return fail(st, "steps[%d]: %s", i, msg.c_str());
+    }
     a.n = st_i.unit->valid;
     a.s = to_device(hs);
   }
   if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  // aligned units go in batches through k_step_multi; the rest one by one
-  MultiArgs batch{};
-  auto flush = [&]() -> fsdp_status {
-    if (batch.nu == 0) return FSDP_OK;
-    batch.n_grads = n_grads;
-    batch.s = to_device(hs);
-    launch_multi(batch, stream);
-    batch = MultiArgs{};
-    return after_launch("fsdp_reduce_adamw_units");
+  // Plan every launch before the first: aligned units of fewer than
+  // kBatchMaxElems shard elements go in batches through k_step_multi, the rest
+  // one by one through the single-unit kernels, in the order given.
+  struct Launch {
+    int32_t batch;    // index into `batches`, or -1 for a single-unit launch
+    int32_t unit;     // index into `args` for a single-unit launch
   };
-  for (int32_t i = 0; i < n_units; ++i) {
-    const StepArgs& a = args[static_cast<size_t>(i)];
-    if (a.n <= 0) continue;
+  std::vector<MultiArgs>& batches = scratch<MultiArgs, 0>();
+  std::vector<Launch>& plan = scratch<Launch, 0>();
+  for (int32_t i = 0; i < int32_t(args.size()); ++i) {
+    const StepArgs& a = args[size_t(i)];
     if (n_grads > kMultiRows || a.n >= kBatchMaxElems ||
         step_path(a, Op::Fused) != Path::Vector) {
-      if (fsdp_status st = launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream,
-                                                  "fsdp_reduce_adamw_units"))
-        return st;
+      plan.push_back(Launch{-1, i});
       continue;
     }
-    UnitDesc& d = batch.u[batch.nu];
+    if (plan.empty() || plan.back().batch < 0 || batches.back().nu == kMaxMultiUnits) {
+      batches.emplace_back();
+      MultiArgs& b = batches.back();
+      b = MultiArgs{};
+      b.n_grads = n_grads;
+      b.s = to_device(hs);
+      plan.push_back(Launch{int32_t(batches.size()) - 1, -1});
+    }
+    MultiArgs& b = batches.back();
+    UnitDesc& d = b.u[b.nu];
     for (int k = 0; k < n_grads; ++k) d.g[k] = a.g[k];
     d.p = a.p;
     d.m = a.m;
     d.v = a.v;
     d.w = a.w;
     d.n = a.n;
-    batch.tiles += (a.n + kStepTile - 1) / kStepTile;
-    d.tile_end = batch.tiles;
-    if (++batch.nu == kMaxMultiUnits)
-      if (fsdp_status st = flush()) return st;
+    b.tiles += (a.n + kStepTile - 1) / kStepTile;
+    d.tile_end = b.tiles;
+    ++b.nu;
   }
-  return flush();
+  if (plan.empty()) return FSDP_OK;               // every window holds only pad
+  if (fsdp_status st = check_no_pending_error(what)) return st;
+  // If the runtime refuses launch k, launches 0..k-1 stay enqueued (documented).
+  for (const Launch& l : plan) {
+    if (l.batch >= 0) {
+      launch_multi(batches[size_t(l.batch)], stream);
+      if (fsdp_status st = after_launch(what)) return st;
+    } else {
+      const StepArgs& a = args[size_t(l.unit)];
+      if (fsdp_status st = launch_step<Op::Fused>(a, step_path(a, Op::Fused), stream, what))
+        return st;
+    }
+  }
+  return FSDP_OK;
 }
 
 fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* const* tensors,
@@ -1316,8 +1359,8 @@ fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* c
   if (!dst) return fail(FSDP_ERR_INVALID_ARG, "dst is NULL");
   if (reinterpret_cast<uintptr_t>(dst) % es)
     return fail(FSDP_ERR_INVALID_ARG, "dst is not element aligned");
-  std::vector<Piece> pieces;
-  std::vector<fsdp::ByteRange> ranges;
+  std::vector<Piece>& pieces = scratch<Piece, 0>();
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
   ranges.push_back(fsdp::range_of(dst, len, es, true, "dst"));
   const int64_t end = begin + len;
   for (int32_t i = 0; i < u->T; ++i) {
@@ -1330,13 +1373,17 @@ fsdp_status fsdp_flatten_pad(const fsdp_unit* u, fsdp_dtype dtype, const void* c
     const char* src = static_cast<const char*>(tensors[i]) + (a - u->offset[i]) * es;
     char* d = static_cast<char*>(dst) + (a - begin) * es;
     pieces.push_back(Piece{src, d, b - a});
-    ranges.push_back(fsdp::range_of(src, b - a, es, false, "tensors[" + std::to_string(i) + "]"));
+    ranges.push_back(fsdp::range_of(src, b - a, es, false, "tensors", i));
   }
   const int64_t pa = std::max(begin, u->U);
   if (pa < end) pieces.push_back(Piece{nullptr, static_cast<char*>(dst) + (pa - begin) * es,
                                        end - pa});
   if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  return launch_pieces(pieces, dtype == FSDP_F32 ? 0 : 1, stream, "fsdp_flatten_pad");
+  const int kind = dtype == FSDP_F32 ? 0 : 1;
+  std::vector<SegArgs>& batches = scratch<SegArgs, 0>();
+  plan_pieces(pieces, kind, &batches);
+  if (fsdp_status st = check_no_pending_error("fsdp_flatten_pad")) return st;
+  return launch_batches(batches, kind, stream, "fsdp_flatten_pad");
 }
 
 fsdp_status fsdp_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype, fsdp_dtype dst_dtype,
@@ -1352,23 +1399,22 @@ fsdp_status fsdp_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype, fsdp_dtype 
   const int64_t ss = src_dtype == FSDP_F32 ? 4 : 2;
   const int64_t ds = dst_dtype == FSDP_F32 ? 4 : 2;
   const int kind = src_dtype == dst_dtype ? (ss == 4 ? 0 : 1) : (src_dtype == FSDP_F32 ? 2 : 3);
-  std::vector<Piece> pieces;
-  std::vector<fsdp::ByteRange> ranges;
+  std::vector<Piece>& pieces = scratch<Piece, 0>();
+  std::vector<fsdp::ByteRange>& ranges = scratch<fsdp::ByteRange, 0>();
   for (int32_t k = 0; k < u->F; ++k) {
     const int64_t kv = std::max<int64_t>(0, std::min<int64_t>(u->S, u->U - k * u->S));
     if (kv == 0) continue;                 // a shard holding only pad is never read
     if (!shards[k]) return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is NULL", k);
     if (reinterpret_cast<uintptr_t>(shards[k]) % ss)
       return fail(FSDP_ERR_INVALID_ARG, "shards[%d] is not element aligned", k);
-    ranges.push_back(fsdp::range_of(shards[k], kv, ss, false, "shards[" + std::to_string(k) + "]"));
+    ranges.push_back(fsdp::range_of(shards[k], kv, ss, false, "shards", k));
   }
   for (int32_t i = 0; i < u->T; ++i) {
     if (u->numel[i] == 0) continue;
     if (!tensors[i]) return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is NULL", i);
     if (reinterpret_cast<uintptr_t>(tensors[i]) % ds)
       return fail(FSDP_ERR_INVALID_ARG, "tensors[%d] is not element aligned", i);
-    ranges.push_back(fsdp::range_of(tensors[i], u->numel[i], ds, true,
-                                    "tensors[" + std::to_string(i) + "]"));
+    ranges.push_back(fsdp::range_of(tensors[i], u->numel[i], ds, true, "tensors", i));
     const int64_t lo = u->offset[i], hi = u->offset[i + 1];
     for (int64_t k = lo / u->S; k * u->S < hi; ++k) {
       const int64_t a = std::max(lo, k * u->S);
@@ -1378,7 +1424,10 @@ fsdp_status fsdp_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype, fsdp_dtype 
     }
   }
   if (fsdp_status st = fsdp::check_alias(ranges)) return st;
-  return launch_pieces(pieces, kind, stream, "fsdp_unflatten");
+  std::vector<SegArgs>& batches = scratch<SegArgs, 0>();
+  plan_pieces(pieces, kind, &batches);
+  if (fsdp_status st = check_no_pending_error("fsdp_unflatten")) return st;
+  return launch_batches(batches, kind, stream, "fsdp_unflatten");
 }
 
 fsdp_status fsdp_cast_unflatten(const fsdp_unit* u, fsdp_dtype src_dtype,

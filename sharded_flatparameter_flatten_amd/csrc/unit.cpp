@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <limits>
 #include <new>
+#include <string>
 
 #include "fsdp_internal.h"
 
@@ -47,12 +48,22 @@ fsdp_status fail(fsdp_status st, const char* fmt, ...) {
 void clear_error() { g_last_error.clear(); }
 
 ByteRange range_of(const void* p, int64_t elems, int64_t elem_bytes, bool write,
-                   const std::string& name) {
+                   const char* label, int32_t index, int32_t unit) {
   uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return ByteRange{lo, lo + static_cast<uintptr_t>(elems * elem_bytes), write, name};
+  return ByteRange{lo, lo + static_cast<uintptr_t>(elems * elem_bytes), write, label, index, unit};
 }
 
-fsdp_status check_alias(std::vector<ByteRange> ranges) {
+namespace {
+std::string range_name(const ByteRange& r) {
+  std::string s;
+  if (r.unit >= 0) s += "unit " + std::to_string(r.unit) + " ";
+  s += r.label;
+  if (r.index >= 0) s += "[" + std::to_string(r.index) + "]";
+  return s;
+}
+}  // namespace
+
+fsdp_status check_alias(std::vector<ByteRange>& ranges) {
   ranges.erase(std::remove_if(ranges.begin(), ranges.end(),
                               [](const ByteRange& r) { return r.hi <= r.lo; }),
                ranges.end());
@@ -66,9 +77,11 @@ fsdp_status check_alias(std::vector<ByteRange> ranges) {
   const ByteRange* last_r = nullptr;
   for (const ByteRange& x : ranges) {
     if (last_w && x.lo < max_hi_w)
-      return fail(FSDP_ERR_ALIAS, "%s overlaps %s", x.name.c_str(), last_w->name.c_str());
+      return fail(FSDP_ERR_ALIAS, "%s overlaps %s", range_name(x).c_str(),
+                  range_name(*last_w).c_str());
     if (x.write && last_r && x.lo < max_hi_r)
-      return fail(FSDP_ERR_ALIAS, "%s overlaps %s", x.name.c_str(), last_r->name.c_str());
+      return fail(FSDP_ERR_ALIAS, "%s overlaps %s", range_name(x).c_str(),
+                  range_name(*last_r).c_str());
     if (x.write) {
       if (!last_w || x.hi > max_hi_w) { max_hi_w = x.hi; last_w = &x; }
     } else {

@@ -226,3 +226,46 @@ def test_hybrid_entry_points_validate_before_launch(lib):
     assert raw.fsdp_reduce_shard_hybrid(u.handle, 2, rows, float("nan"), p, None) == 1
     win = FAKE + 5 * (1 << 20) + 2 * u.shard_begin
     assert raw.fsdp_reduce_shard_hybrid(u.handle, 2, rows, 0.0625, win, None) == 3
+
+
+def test_empty_window_needs_no_buffers(lib):
+    """A rank whose window holds only pad (shard_valid 0): the step calls check their
+    counts and hyper-parameters and return ok without touching their buffers."""
+    raw = _raw(lib)
+    u = lib.Unit([(5,)], 8, 6)
+    assert u.shard_valid == 0
+    hp = ctypes.byref(_hp(lib))
+    assert raw.fsdp_reduce_adamw_shard(u.handle, 8, None, None, None, None, None, hp, None) == 0
+    assert raw.fsdp_reduce_shard(u.handle, 8, None, 0.125, None, None) == 0
+    assert raw.fsdp_adamw_shard(u.handle, None, None, None, None, None, hp, None) == 0
+    assert raw.fsdp_reduce_adamw_shard_bf16acc(u.handle, 8, None, None, None, None, None, hp,
+                                               None) == 0
+    assert raw.fsdp_reduce_adamw_shard_hybrid(u.handle, 2, None, None, None, None, None, hp,
+                                              None) == 0
+    # counts and hyper-parameters are still checked
+    assert raw.fsdp_reduce_adamw_shard(u.handle, 0, None, None, None, None, None, hp, None) == 1
+    assert raw.fsdp_reduce_adamw_shard(u.handle, 8, None, None, None, None, None,
+                                       ctypes.byref(_hp(lib, step=0)), None) == 1
+    assert raw.fsdp_reduce_adamw_shard_hybrid(u.handle, 9, None, None, None, None, None, hp,
+                                              None) == 1
+    arr = (lib._UnitStep * 1)(lib._UnitStep(u.handle.value, None, None, None, None, None))
+    assert raw.fsdp_reduce_adamw_units(1, arr, 8, hp, None) == 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="needs a HIP runtime with no usable device (the CPU container)")
+def test_pending_runtime_error_is_reported_before_any_launch(lib):
+    """Without a usable device the HIP runtime holds an error from its start-up; a call
+    with valid arguments reports it as pending (FSDP_ERR_HIP) and launches nothing."""
+    raw = _raw(lib)
+    u = lib.Unit([(4096,)], 8, 3)
+    arr = lib._ptr_array([FAKE + k * (1 << 20) for k in range(8)])
+    p, m, v = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    hp = ctypes.byref(_hp(lib))
+    for call in (lambda: raw.fsdp_reduce_adamw_shard(u.handle, 8, arr, p, m, v, None, hp, None),
+                 lambda: raw.fsdp_reduce_shard(u.handle, 8, arr, 0.125, p, None),
+                 lambda: raw.fsdp_flatten_pad(u.handle, 0, lib._ptr_array([FAKE]), 0, 512, p,
+                                              None)):
+        assert call() == 5
+        msg = raw.fsdp_last_error().decode()
+        assert "pending" in msg and "nothing was enqueued" in msg, msg
