@@ -496,7 +496,8 @@ def model_sequence(args):
 
 def sharding_sweep(args):
     """Fused reduce+AdamW+emit on ranks 0 and F-1 of the 7B block for each F of the sweep,
-    visiting `--rotate` independent buffer sets in turn."""
+    visiting `--rotate` independent buffer sets in turn (gradient rows laid out as
+    --row-layout says)."""
     import torch
 
     import datagen
@@ -515,7 +516,8 @@ def sharding_sweep(args):
     for F in Fs:
         for rank in sorted({0, F - 1}):
             u = fsdp.Unit(shapes, F, rank)
-            rows = rotating_rows(torch, datagen, W, u, F, R, dev, gseed, outlier_seed=oseed)
+            rows = rotating_rows(torch, datagen, W, u, F, R, dev, gseed, outlier_seed=oseed,
+                                 separate=args.row_layout == "separate")
             state = []
             for j in range(R):
                 p = torch.empty(u.S, dtype=torch.float32, device=dev)
@@ -543,6 +545,7 @@ def sharding_sweep(args):
             nbytes = (2 * F + 26) * u.shard_valid
             out.append({"F": F, "rank": rank, "S": u.S, "valid": u.shard_valid,
                         "row_path": "vector" if (2 * u.shard_begin) % 8 == 0 else "shifted",
+                        "row_layout": args.row_layout,
                         "rotating_sets": R,
                         "fused_us_avg": avg, "fused_us_median": us[len(us) // 2],
                         "bytes": nbytes, "GBps": nbytes / (avg * 1e-6) / 1e9,
@@ -861,7 +864,8 @@ def main():
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
     ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],
-                    help="blk7: one allocation per gradient row, or all rows' windows in one arena")
+                    help="blk7, sweep: one allocation per gradient row (each rank's gradient "
+                         "its own buffer), or all rows' windows in one arena")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
                     help="blk7: only the headline steps and the two 1 GiB reference copies "

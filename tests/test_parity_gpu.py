@@ -611,7 +611,8 @@ def test_hybrid_fused_every_rank_every_element(R, F):
             assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"R={R} F={F} r={rank} {name}")
 
 
-@pytest.mark.parametrize("R,F,rank", [(2, 4, 1), (3, 7, 3)])      # F=7: odd S, scalar path
+@pytest.mark.parametrize("R,F,rank", [(2, 4, 1), (3, 7, 3),      # F=7: odd S, scalar path
+                                      (2, 8, 5)])                 # compile-time 2 x 8 fold
 def test_hybrid_reduce_shard_every_element(R, F, rank):
     shapes = [(2049,), (7, 9)]
     case = Case(shapes, F, rank, config=31, replicas=R)
@@ -645,7 +646,8 @@ def test_hybrid_blk7_two_groups_of_8_sampled():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("shapes,F,ng", [([(1000, 7), (33,)], 4, 4), ([(1000, 7), (33,)], 8, 8),
-                                         ([(5000,)], 4, 12), ([(1000, 3), (17,)], 7, 7)])
+                                         ([(5000,)], 4, 12), ([(1000, 3), (17,)], 7, 7),
+                                         ([(1000, 7), (33,)], 8, 16)])
 def test_bf16acc_fused_every_rank_every_element(shapes, F, ng):
     for rank in range(F):
         case = Case(shapes, F, rank, n_grads=ng, config=40, outliers=True, bf16acc=True)
@@ -663,9 +665,10 @@ def test_bf16acc_fused_every_rank_every_element(shapes, F, ng):
             assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"bf16acc F={F} r={rank} {name}")
 
 
-def test_bf16acc_reduce_shard_every_element_and_coarser_than_fp32():
+@pytest.mark.parametrize("ng", [4, 8, 16])       # 8 and 16: the compile-time folds
+def test_bf16acc_reduce_shard_every_element_and_coarser_than_fp32(ng):
     shapes, F, rank = [(4096, 5)], 4, 2
-    case = Case(shapes, F, rank, config=41, outliers=True, bf16acc=True)
+    case = Case(shapes, F, rank, n_grads=ng, config=41, outliers=True, bf16acc=True)
     u = fsdp.Unit(shapes, F, rank)
     grads = case.device_grads(1)
     out = torch.empty(u.S, dtype=torch.float32, device=DEV)
@@ -691,6 +694,31 @@ def test_bf16acc_blk7_sampled():
     want = case.oracle_sampled(loc, 1)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
         assert_bits(_bits(gather(got, loc)), _bits(exp), f"bf16acc blk7 {name}")
+
+
+def test_unfused_long_launch_sampled():
+    """fsdp_reduce_shard then fsdp_adamw_shard on a 202,383,360-element shard (the 7B
+    block at F=1, 8 gradient rows): the 128-thread workgroups of launches of 2^25+
+    elements, with the stand-alone AdamW kernel capped; sampled indices against the
+    oracle, two steps."""
+    case = Case(W.shapes(W.BLK7), 1, 0, n_grads=8, config=44)
+    u = fsdp.Unit(case.shapes, 1, 0)
+    assert u.shard_valid >= 1 << 25
+    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.flatten_pad(u, case.device_master_tensors(), p)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    g32 = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    grads = None
+    for t in (1, 2):
+        grads = case.device_grads(t, out=grads)
+        fsdp.reduce_shard(u, grads, g32)
+        fsdp.adamw_shard(u, g32, p, m, v, w, HPD, t)
+    torch.cuda.synchronize()
+    loc = case.sample_indices()
+    want = case.oracle_sampled(loc, 2)[-1]
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(gather(got, loc)), _bits(exp), f"unfused F=1 {name}")
 
 
 def test_sharded_steps_concatenated_equal_the_ddp_step():
