@@ -219,6 +219,58 @@ def cpu_baseline(F: int, rank: int, sample: int, budget_s: float):
     return res
 
 
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, with the
+    record / elapsed_time interface of torch.cuda.Event.
+
+    torch's events record with a system-scope fence (cache write-back and
+    invalidation when the event completes); HIP documents disabling it for
+    events used only to measure time, as it improves the accuracy of the
+    measurement on AMD GPUs and costs the stream less. Measured on the 7B-block
+    step: the fused kernel's event interval is 166.0 us with these events and
+    167.3 us with torch's, against 163.5 us of kernel time in a rocprofv3 trace
+    of the same loop."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        st = self._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream=None):
+        import torch
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        st = self._hip.hipEventRecord(self.h, self._ct.c_void_p(s))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._ct.c_float()
+        st = self._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+            self.h = None
+
+
 def spread(ms):
     """Average, median, 10th and 90th percentile and minimum of event intervals, in us."""
     xs = sorted(x * 1e3 for x in ms)
@@ -307,7 +359,7 @@ def make_sets(fsdp, torch, datagen, W, units, rank, R, dev, separate=True, keep_
 def bracketed_steps(torch, stream, fused, gather, first, L):
     """L steps (fused, then gather) with each kernel bracketed by HIP events on
     `stream`; returns the fused and gather intervals in ms."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
+    ev = [[TimingEvent() for _ in range(3)] for _ in range(L)]
     torch.cuda.synchronize()
     for i in range(L):
         ev[i][0].record(stream)
@@ -366,7 +418,7 @@ def copy_reference(fsdp, torch, dev, stream, reps=10):
     dst = torch.empty_like(src)
     for _ in range(2):
         fsdp.flatten_pad(cu, [src], dst, stream=stream)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = TimingEvent(), TimingEvent()
     c0.record(stream)
     for _ in range(reps):
         fsdp.flatten_pad(cu, [src], dst, stream=stream)
@@ -381,7 +433,7 @@ def torch_copy_reference(torch, dev, reps=2):
     src = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = TimingEvent(), TimingEvent()
     c0.record()
     for _ in range(reps):
         dst.copy_(src)
@@ -467,7 +519,7 @@ def model_sequence(args):
         step(i + 1)
     torch.cuda.synchronize()
     K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = TimingEvent(), TimingEvent()
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(K):
@@ -534,7 +586,7 @@ def sharding_sweep(args):
             for i in range(W0):
                 fused(i)
             K = max(args.steps, 2 * R)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+            ev = [TimingEvent() for _ in range(K + 1)]
             ev[0].record(stream)
             for i in range(K):
                 fused(W0 + i)
@@ -588,7 +640,7 @@ def hybrid_bench(args):
         for i in range(max(args.warmup, R)):
             fn(i)
         K = max(args.steps, 2 * R)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for i in range(K):
             fn(i)
@@ -648,7 +700,7 @@ def state_dict_bench(args):
         for i in range(max(args.warmup, R)):
             fn(i)
         K = max(args.steps, 2 * R)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for i in range(K):
             fn(i)
@@ -944,7 +996,7 @@ def main():
     K = args.steps
     N = max(1, args.event_every)
     sampled = [i for i in range(K) if i % N == 0]
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    ev = {i: [TimingEvent() for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -1024,7 +1076,7 @@ def main():
     def timed(fn, reps):
         for i in range(R):
             fn(i)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(stream)
         for i in range(reps):
             fn(i)

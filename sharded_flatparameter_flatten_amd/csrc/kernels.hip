@@ -522,7 +522,7 @@ template <Op OP, int NG, bool EMIT>
 __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   static_assert(OP != Op::AdamW, "only the gradient rows are shifted");
   constexpr int V = 4;
-  constexpr int64_t TILE = int64_t(kStepThreads) * V;
+  const int64_t TILE = int64_t(blockDim.x) * V;          // 64, 128 or 256 threads
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * TILE;
   for (int64_t t0 = int64_t(blockIdx.x) * TILE; t0 < n; t0 += stride) {
@@ -891,14 +891,11 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, size_t lds, hi
   }
 }
 template <Op OP, bool EMIT>
-void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
-  // 256-thread workgroups, capped like the vector path's 256-thread form
-  const bool cap = a.n >= (int64_t(1) << FSDP_CAP_MIN_LOG2);
-  const int base = OP == Op::Reduce ? FSDP_REDUCE_WG_PER_CU : FSDP_FUSED_WG_PER_CU;
-  const size_t lds = cap ? lds_reservation(base) : 0;
+void launch_shift_ng(const StepArgs& a, unsigned grid, int threads, size_t lds,
+                     hipStream_t stream) {
   switch (a.n_grads) {
 #define FSDP_NG_CASE(K) \
-  case K: k_step_shift<OP, K, EMIT><<<grid, kStepThreads, lds, stream>>>(a); break;
+  case K: k_step_shift<OP, K, EMIT><<<grid, threads, lds, stream>>>(a); break;
     FSDP_NG_CASE(1)
     FSDP_NG_CASE(2)
     FSDP_NG_CASE(3)
@@ -909,7 +906,7 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, hipStream_t stream) {
     FSDP_NG_CASE(8)
     FSDP_NG_CASE(16)
 #undef FSDP_NG_CASE
-    default: k_step_shift<OP, 0, EMIT><<<grid, kStepThreads, (cap && OP == Op::Reduce ? lds : 0), stream>>>(a); break;
+    default: k_step_shift<OP, 0, EMIT><<<grid, threads, lds, stream>>>(a); break;
   }
 }
 
@@ -927,9 +924,13 @@ fsdp_status launch_step(const StepArgs& a, Path path, hipStream_t stream, const 
     else launch_vec_ng<OP, false>(a, grid, sh.threads, lds, stream);
   } else if (path == Path::Shifted) {
     if constexpr (OP != Op::AdamW) {
-      const unsigned grid = grid_for((a.n + 4 * kStepThreads - 1) / (4 * kStepThreads));
-      if (a.w) launch_shift_ng<OP, true>(a, grid, stream);
-      else launch_shift_ng<OP, false>(a, grid, stream);
+      // the same occupancy plan as the vector path (the shifted path only folds flat)
+      const Shape sh = step_shape<OP>(a);
+      const int64_t tile = int64_t(sh.threads) * 4;
+      const unsigned grid = grid_for((a.n + tile - 1) / tile);
+      const size_t lds = lds_reservation(sh.wg_per_cu);
+      if (a.w) launch_shift_ng<OP, true>(a, grid, sh.threads, lds, stream);
+      else launch_shift_ng<OP, false>(a, grid, sh.threads, lds, stream);
     }
   } else {
     const unsigned grid = grid_for((a.n + kStepTile - 1) / kStepTile);

@@ -149,13 +149,15 @@ def test_grouped_fold_guards(lib, kind):
         t.check(f"{kind} {nm}")
 
 
-def test_long_launch_guards(lib):
-    """The one-wave-workgroup shape (8 rows, 2^24 + 3 elements: a ragged last tile):
-    the guards around the windows and the elements at both ends."""
+@pytest.mark.parametrize("rank", [0, 1], ids=["vector_rows", "shifted_rows"])
+def test_long_launch_guards(lib, rank):
+    """The one-wave-workgroup shape (8 rows, 2^24 + 3 elements: a ragged last tile),
+    with aligned gradient windows (rank 0) and windows at a 6-byte offset (rank 1: the
+    shifted-row path): the guards around the windows and the elements at both ends."""
     F, S = 8, (1 << 24) + 3
-    u = lib.Unit([(F * S,)], F, 0)
+    u = lib.Unit([(F * S,)], F, rank)
     n = u.shard_valid
-    assert n == S
+    assert n == S and ((2 * u.shard_begin) % 8 == 0) == (rank == 0)
     rows = rows_for(u, F)
     p, m, v = state_for(n)
     w = Guarded(n, torch.bfloat16)
