@@ -813,12 +813,13 @@ size_t lds_reservation(int wg_per_cu) {
 // workgroups per CU (0: as many as fit). Chosen by measurement on MI355X
 // (rotating buffer sets, several boxes and allocations):
 //  * launches under 2^23 elements run every workgroup they have at once;
-//  * the fused step with a compile-time fold of at least FSDP_SMALL_WG_MIN_ROWS
-//    rows, on 2^FSDP_SMALL_WG_MIN_LOG2 elements or more, runs one-wave
-//    workgroups (256-element tiles), 8 per CU: each lane then has 8n+48 bytes
-//    of loads in flight, and 8 waves per CU keep enough bytes in flight while
-//    the small tiles keep the write streams of one CU short and the tail of
-//    the launch short;
+//  * the fused step with a compile-time flat fold (one group, fp32 partials) of
+//    at least FSDP_SMALL_WG_MIN_ROWS rows, on 2^FSDP_SMALL_WG_MIN_LOG2 elements
+//    or more, runs one-wave workgroups (256-element tiles), 8 per CU: each lane
+//    then has 8n+48 bytes of loads in flight, and 8 waves per CU keep enough
+//    bytes in flight while the small tiles keep the write streams of one CU
+//    short and the tail of the launch short (the grouped folds measured no
+//    faster in this shape and keep the 256-thread one);
 //  * other launches of 2^FSDP_HALF_TILE_MIN_LOG2 elements or more run
 //    128-thread workgroups, with the per-CU count of their 256-thread form
 //    doubled (same waves per CU);
