@@ -385,7 +385,8 @@ def stream_mix_leg(torch, stream, sets, u, rank, F, gather, first, L):
     lib.probe_stream_mix.restype = ctypes.c_int
     lib.probe_stream_mix.argtypes = [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_void_p] * 4 + \
         [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    # the library's shape for this launch: one-wave workgroups, 8 per CU
+    # the library's shape for this launch: one-wave workgroups, as many per CU as
+    # 1280 bytes over the 168 bytes a lane moves per tile (8 rows + state + bf16)
     threads, wg_per_cu = 64, 8
     R = len(sets)
     rows = []

@@ -21,13 +21,12 @@
 //    back while the next kernel ran and slowed it; the streaming stores
 //    finish inside the kernel that issues them, and the 7B-block step
 //    (fused + gather) went from ~318 us to ~307 us;
-//  * occupancy, also chosen by measurement (step_shape below): long fused
-//    launches with a compile-time fold of 4+ gradient rows run one-wave
-//    workgroups (256-element tiles), 8 per CU; other long launches of the
-//    fused kernels with a compile-time row count and of the stand-alone AdamW
-//    kernel run 12 waves per CU (3 workgroups of 256 threads, or 6 of 128
-//    threads at 2^25+ elements); the per-CU counts are held down by unused
-//    dynamic LDS sized from the device's LDS per CU;
+//  * occupancy, also chosen by measurement (step_shape below): long launches
+//    of the reduce, AdamW and fused kernels run one-wave workgroups
+//    (256-element tiles), as many per CU as keep about 80 KiB of loads and
+//    stores in flight per CU (8 for the fused step with 8 rows); the per-CU
+//    counts are held down by unused dynamic LDS sized from the device's LDS
+//    per CU;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
@@ -80,42 +79,27 @@
 #define FSDP_COPY_STORE_CPOL 18
 #endif
 
-// Resident 256-thread step workgroups per CU (0: no cap). The cap is imposed
-// with unused dynamic LDS, and only on launches of at least 2^FSDP_CAP_MIN_LOG2
-// elements: a shorter launch has fewer tiles than a few rounds of a full
-// machine and runs best with every workgroup resident.
-#ifndef FSDP_REDUCE_WG_PER_CU
-#define FSDP_REDUCE_WG_PER_CU 0
-#endif
-#ifndef FSDP_ADAMW_WG_PER_CU
-#define FSDP_ADAMW_WG_PER_CU 3
-#endif
+// Resident 256-thread workgroups per CU of the step kernels that keep that
+// shape (0: no cap), imposed with unused dynamic LDS and only on launches of
+// at least 2^FSDP_CAP_MIN_LOG2 elements (see step_shape).
 #ifndef FSDP_FUSED_WG_PER_CU
-#define FSDP_FUSED_WG_PER_CU 3
+#define FSDP_FUSED_WG_PER_CU 3      // the compile-time grouped folds
 #endif
 #ifndef FSDP_MULTI_WG_PER_CU
-#define FSDP_MULTI_WG_PER_CU 3    // the batched many-unit fused kernel
+#define FSDP_MULTI_WG_PER_CU 3      // the batched many-unit fused kernel
 #endif
 #ifndef FSDP_CAP_MIN_LOG2
-#define FSDP_CAP_MIN_LOG2 23       // launches of 2^23+ elements are capped
+#define FSDP_CAP_MIN_LOG2 23
 #endif
-// Single-unit step launches of at least 2^FSDP_HALF_TILE_MIN_LOG2 elements use
-// 128-thread workgroups (512-element tiles), with the workgroup cap doubled so
-// that a CU holds the same number of waves.
+// Grouped-fold launches of at least 2^FSDP_HALF_TILE_MIN_LOG2 elements use
+// 128-thread workgroups, with the per-CU count doubled (the same waves per CU).
 #ifndef FSDP_HALF_TILE_MIN_LOG2
 #define FSDP_HALF_TILE_MIN_LOG2 25
 #endif
-// Fused launches with a compile-time flat fold of at least FSDP_SMALL_WG_MIN_ROWS
-// rows on 2^FSDP_SMALL_WG_MIN_LOG2+ elements: one-wave workgroups, at most
-// FSDP_SMALL_WG_PER_CU per CU.
-#ifndef FSDP_SMALL_WG_MIN_LOG2
-#define FSDP_SMALL_WG_MIN_LOG2 24
-#endif
-#ifndef FSDP_SMALL_WG_MIN_ROWS
-#define FSDP_SMALL_WG_MIN_ROWS 4
-#endif
-#ifndef FSDP_SMALL_WG_PER_CU
-#define FSDP_SMALL_WG_PER_CU 8
+// Bytes each lane of a one-wave workgroup should have moving per CU slot (see
+// step_shape): one-wave workgroups per CU = FSDP_LANE_BUDGET / lane bytes.
+#ifndef FSDP_LANE_BUDGET
+#define FSDP_LANE_BUDGET 1280
 #endif
 
 using fsdp::fail;
@@ -809,24 +793,30 @@ size_t lds_reservation(int wg_per_cu) {
   return 0;
 }
 
-// Occupancy plan of a vector-path step launch: workgroup size and resident
-// workgroups per CU (0: as many as fit). Chosen by measurement on MI355X
-// (rotating buffer sets, several boxes and allocations):
-//  * launches under 2^23 elements run every workgroup they have at once;
-//  * the fused step with a compile-time flat fold (one group, fp32 partials) of
-//    at least FSDP_SMALL_WG_MIN_ROWS rows, on 2^FSDP_SMALL_WG_MIN_LOG2 elements
-//    or more, runs one-wave workgroups (256-element tiles), 8 per CU: each lane
-//    then has 8n+48 bytes of loads in flight, and 8 waves per CU keep enough
-//    bytes in flight while the small tiles keep the write streams of one CU
-//    short and the tail of the launch short (the grouped folds measured no
-//    faster in this shape and keep the 256-thread one);
-//  * other launches of 2^FSDP_HALF_TILE_MIN_LOG2 elements or more run
-//    128-thread workgroups, with the per-CU count of their 256-thread form
-//    doubled (same waves per CU);
-//  * the stand-alone AdamW kernel and the fused kernels with a compile-time
-//    fold run at most 3 workgroups of 256 threads per CU (12 waves); the
-//    fused kernels that walk a run-time row count in dependent chunks, and
-//    the reduce-only kernel, are never capped.
+// Occupancy plan of a vector-path (and shifted-path) step launch: workgroup
+// size and resident workgroups per CU (0: as many as fit). Chosen by
+// measurement on MI355X (rotating buffer sets, each variant on the same
+// buffers, several boxes and allocations):
+//  * launches under 2^FSDP_CAP_MIN_LOG2 elements run 256-thread workgroups, all
+//    resident at once: they have fewer tiles than a few rounds of the machine;
+//  * the reduce, the stand-alone AdamW and the fused kernels with a
+//    compile-time flat fold run one-wave workgroups (64 threads, 256-element
+//    tiles), with the per-CU count set so that a CU keeps about
+//    FSDP_LANE_BUDGET * 64 bytes of loads and stores in flight: count =
+//    round(FSDP_LANE_BUDGET / bytes a lane moves per tile), within [8, 32]. A
+//    lane moves 8 bytes per gradient row and 16 bytes per fp32 array, read or
+//    written (and 8 for the bf16 output): the fused step with 8 rows and the
+//    emission moves 168 bytes (8 per CU), the stand-alone AdamW 120 (11), the
+//    reduce of 8 rows 80 (16), of 2 rows 32 (32). Little's law gives the same
+//    size: a CU's 1/256 share of 8 TB/s over a loaded latency of a few
+//    microseconds. The one-wave tiles keep each CU's write streams short and
+//    the end of a launch short;
+//  * the compile-time grouped folds (hybrid sharding, bf16 partial sums), which
+//    measured no faster in that shape, run 256-thread workgroups, at most
+//    FSDP_FUSED_WG_PER_CU per CU (12 waves) when fused, or 128-thread ones at
+//    2^FSDP_HALF_TILE_MIN_LOG2+ elements with the count doubled;
+//  * the fused kernels that walk a run-time row count in dependent chunks are
+//    never capped (256 threads).
 struct Shape {
   int threads;
   int wg_per_cu;
@@ -841,18 +831,26 @@ bool compile_time_fold(const StepArgs& a) {
   return (a.n_grads >= 1 && a.n_grads <= 8) || a.n_grads == 16;
 }
 
+// Bytes one lane (4 consecutive elements) reads and writes per tile.
+template <Op OP>
+int lane_bytes(const StepArgs& a) {
+  const int w = a.w ? 8 : 0;
+  if (OP == Op::Reduce) return 8 * a.n_grads + 16;
+  if (OP == Op::AdamW) return 16 + 48 + 48 + w;
+  return 8 * a.n_grads + 96 + w;
+}
+
 template <Op OP>
 Shape step_shape(const StepArgs& a) {
-  const bool fixed = OP != Op::AdamW && compile_time_fold(a);
-  const bool flat = a.group == a.n_grads && !a.bf16acc;
-  const int base = OP == Op::Reduce  ? FSDP_REDUCE_WG_PER_CU
-                 : OP == Op::AdamW ? FSDP_ADAMW_WG_PER_CU
-                 : fixed           ? FSDP_FUSED_WG_PER_CU
-                                   : 0;
   if (a.n < (int64_t(1) << FSDP_CAP_MIN_LOG2)) return Shape{kStepThreads, 0};
-  if (OP == Op::Fused && fixed && flat && a.n_grads >= FSDP_SMALL_WG_MIN_ROWS &&
-      a.n >= (int64_t(1) << FSDP_SMALL_WG_MIN_LOG2))
-    return Shape{kSmallThreads, FSDP_SMALL_WG_PER_CU};
+  const bool flat = a.group == a.n_grads && !a.bf16acc;
+  if (OP == Op::AdamW || (flat && compile_time_fold(a))) {
+    const int b = lane_bytes<OP>(a);
+    const int wg = std::min(32, std::max(8, (FSDP_LANE_BUDGET + b / 2) / b));
+    return Shape{kSmallThreads, wg};
+  }
+  if (!compile_time_fold(a)) return Shape{kStepThreads, 0};
+  const int base = OP == Op::Reduce ? 0 : FSDP_FUSED_WG_PER_CU;   // reduce-only: uncapped
   if (a.n >= (int64_t(1) << FSDP_HALF_TILE_MIN_LOG2)) return Shape{kStepThreads / 2, 2 * base};
   return Shape{kStepThreads, base};
 }

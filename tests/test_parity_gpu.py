@@ -698,9 +698,9 @@ def test_bf16acc_blk7_sampled():
 
 def test_unfused_long_launch_sampled():
     """fsdp_reduce_shard then fsdp_adamw_shard on a 202,383,360-element shard (the 7B
-    block at F=1, 8 gradient rows): the 128-thread workgroups of launches of 2^25+
-    elements, with the stand-alone AdamW kernel capped; sampled indices against the
-    oracle, two steps."""
+    block at F=1, 8 gradient rows): the one-wave workgroups of long launches, 16 per CU
+    for this reduce and 11 for the AdamW; sampled indices against the oracle, two
+    steps."""
     case = Case(W.shapes(W.BLK7), 1, 0, n_grads=8, config=44)
     u = fsdp.Unit(case.shapes, 1, 0)
     assert u.shard_valid >= 1 << 25
