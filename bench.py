@@ -550,7 +550,7 @@ def model_sequence(args):
 def sharding_sweep(args):
     """Fused reduce+AdamW+emit on ranks 0 and F-1 of the 7B block for each F of the sweep,
     visiting `--rotate` independent buffer sets in turn (gradient rows laid out as
-    --row-layout says)."""
+    --row-layout says; "both": each rank in the separate layout, then in the arena)."""
     import torch
 
     import datagen
@@ -566,11 +566,12 @@ def sharding_sweep(args):
     hp = fsdp.AdamWHparams(**W.ADAMW)
     stream = torch.cuda.current_stream(dev)
     out = []
-    for F in Fs:
-        for rank in sorted({0, F - 1}):
+    layouts = ["separate", "arena"] if args.row_layout == "both" else [args.row_layout]
+    for F, rank, layout in ((F, rank, layout) for F in Fs for rank in sorted({0, F - 1})
+                            for layout in layouts):
             u = fsdp.Unit(shapes, F, rank)
             rows = rotating_rows(torch, datagen, W, u, F, R, dev, gseed, outlier_seed=oseed,
-                                 separate=args.row_layout == "separate")
+                                 separate=layout == "separate")
             state = []
             for j in range(R):
                 p = torch.empty(u.S, dtype=torch.float32, device=dev)
@@ -598,7 +599,7 @@ def sharding_sweep(args):
             nbytes = (2 * F + 26) * u.shard_valid
             out.append({"F": F, "rank": rank, "S": u.S, "valid": u.shard_valid,
                         "row_path": "vector" if (2 * u.shard_begin) % 8 == 0 else "shifted",
-                        "row_layout": args.row_layout,
+                        "row_layout": layout,
                         "rotating_sets": R,
                         "fused_us_avg": avg, "fused_us_median": us[len(us) // 2],
                         "bytes": nbytes, "GBps": nbytes / (avg * 1e-6) / 1e9,
@@ -916,9 +917,10 @@ def main():
                          "one allocation per array, or each unit's arrays allocated on their own")
     ap.add_argument("--per-unit", action="store_true",
                     help="whole-model workloads: one launch per unit instead of batched")
-    ap.add_argument("--row-layout", default="separate", choices=["separate", "arena"],
+    ap.add_argument("--row-layout", default="separate", choices=["separate", "arena", "both"],
                     help="blk7, sweep: one allocation per gradient row (each rank's gradient "
-                         "its own buffer), or all rows' windows in one arena")
+                         "its own buffer), or all rows' windows in one arena; sweep only: "
+                         "both, one after the other")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true",
                     help="blk7: only the headline steps and the two 1 GiB reference copies "
@@ -926,6 +928,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1 << 22)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     args = ap.parse_args()
+    if args.row_layout == "both" and args.workload != "sweep":
+        ap.error("--row-layout both applies to --workload sweep only")
 
     if args.gpus != 1:
         print(f"bench.py measures one rank's shard step on one GPU; --gpus {args.gpus} is not "

@@ -79,22 +79,15 @@
 #define FSDP_COPY_STORE_CPOL 18
 #endif
 
-// Resident 256-thread workgroups per CU of the step kernels that keep that
-// shape (0: no cap), imposed with unused dynamic LDS and only on launches of
-// at least 2^FSDP_CAP_MIN_LOG2 elements (see step_shape).
-#ifndef FSDP_FUSED_WG_PER_CU
-#define FSDP_FUSED_WG_PER_CU 3      // the compile-time grouped folds
-#endif
+// Resident 256-thread workgroups per CU of the batched many-unit fused kernel
+// (0: no cap), imposed with unused dynamic LDS on batches of at least
+// 2^FSDP_CAP_MIN_LOG2 elements; the single-unit step launches of that size
+// take their shape from step_shape.
 #ifndef FSDP_MULTI_WG_PER_CU
-#define FSDP_MULTI_WG_PER_CU 3      // the batched many-unit fused kernel
+#define FSDP_MULTI_WG_PER_CU 3
 #endif
 #ifndef FSDP_CAP_MIN_LOG2
 #define FSDP_CAP_MIN_LOG2 23
-#endif
-// Grouped-fold launches of at least 2^FSDP_HALF_TILE_MIN_LOG2 elements use
-// 128-thread workgroups, with the per-CU count doubled (the same waves per CU).
-#ifndef FSDP_HALF_TILE_MIN_LOG2
-#define FSDP_HALF_TILE_MIN_LOG2 25
 #endif
 // Bytes each lane of a one-wave workgroup should have moving per CU slot (see
 // step_shape): one-wave workgroups per CU = FSDP_LANE_BUDGET / lane bytes.
@@ -186,15 +179,6 @@ __device__ __forceinline__ void accumulate(u32x2 q, float (&x)[4]) {
   x[2] = x[2] + lo_bf16(q.y); x[3] = x[3] + hi_bf16(q.y);
 }
 
-template <int SV>
-__device__ __forceinline__ void loadf(const float* p, float (&x)[SV]) {
-#pragma unroll
-  for (int h = 0; h < SV / 4; ++h) {
-    const f32x4 a = ldh<f32x4, kStateNt>(p + 4 * h);
-    x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
-  }
-}
-
 // Buffer descriptor over [base, base + bytes) with the gfx9 raw-buffer format
 // word; a store beyond it is dropped by the hardware.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -208,6 +192,36 @@ __device__ __forceinline__ void bst(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) 
 template <int CP>
 __device__ __forceinline__ void bst(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CP);
+}
+
+// Where a lane's accesses of one tile start: the tile's first element t0 and
+// its length (both workgroup-uniform) and the lane's element offset within
+// the tile. A load is a buffer load through a descriptor over the tile, so
+// its base stays in scalar registers and the lane adds a 32-bit byte offset
+// (no 64-bit address arithmetic per row in vector registers, which otherwise
+// limits how many loads the compiler keeps in flight).
+struct At {
+  int64_t t0;
+  int64_t len;
+  uint32_t off;
+};
+// present == false: a zero-length descriptor, so the load reads no memory and
+// returns zeros.
+template <typename V, bool NT, typename T>
+__device__ __forceinline__ V ld_tile(const T* base, At at, bool present = true) {
+  const __amdgpu_buffer_rsrc_t r =
+      rsrc(const_cast<T*>(base) + at.t0, present ? int64_t(sizeof(T)) * at.len : 0);
+  const int off = int(at.off * uint32_t(sizeof(T)));
+  constexpr int cp = NT ? 2 : 0;   // 2: nt (streaming)
+  if constexpr (sizeof(V) == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, cp);
+  else return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, cp);
+}
+
+// A lane's 4 consecutive fp32 values of a tile.
+__device__ __forceinline__ void loadf(const float* base, At at, float (&x)[4]) {
+  const u32x4 a = ld_tile<u32x4, kStateNt>(base, at);
+  x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+  x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
 }
 
 // One lane's 4 results at element i of a workgroup tile that starts at
@@ -249,31 +263,51 @@ struct StepArgs {
 
 enum class Op { Reduce, AdamW, Fused };
 
-// Left fold of the gradient rows for SV consecutive elements at i, times gs.
-// NG > 0 is the compile-time count (all loads issued before the first add);
-// NG == 0 reads the count at run time and walks the rows in chunks of 8.
+// Left fold of the gradient rows for SV consecutive elements of a tile,
+// times gs. NG > 0 is the compile-time count: every row load is issued (and
+// held issued by a scheduling barrier) before the first add. NG == 0 reads the
+// count at run time and folds chunks of 8 rows, each chunk's loads issued
+// before its first add. That fold starts from -0.0, the exact identity of IEEE
+// addition (-0 + x is x for every x, -0, infinities and NaN included), so its
+// sums are those of the fold that starts from the first row; in the last,
+// partial chunk the rows past the count load nothing (a zero-length
+// descriptor) and add -0.0. Reading g[k + j] there stays inside the array: the
+// chunk starts at a multiple of 8 below n_grads <= FSDP_MAX_RANKS, so its last
+// pointer is below FSDP_MAX_RANKS.
 template <int NG, int SV>
 __device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, float gs,
-                                            int64_t i, float (&acc)[SV]) {
+                                            At at, float (&acc)[SV]) {
   using G = u32x2;
   if constexpr (NG > 0) {
     G q[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) q[k] = ldh<G, kGradNt>(g[k] + i);
+    for (int k = 0; k < NG; ++k) q[k] = ld_tile<G, kGradNt>(g[k], at);
+    __builtin_amdgcn_sched_barrier(0);
     unpack(q[0], acc);
 #pragma unroll
     for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
   } else {
-    unpack(ldh<G, kGradNt>(g[0] + i), acc);
-    int k = 1;
+    static_assert(FSDP_MAX_RANKS % 8 == 0, "whole chunks of row pointers");
+#pragma unroll
+    for (int e = 0; e < SV; ++e) acc[e] = -0.0f;
+    int k = 0;
     for (; k + 8 <= ng; k += 8) {
       G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(g[k + j] + i);
+      for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[k + j], at);
 #pragma unroll
       for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
     }
-    for (; k < ng; ++k) accumulate(ldh<G, kGradNt>(g[k] + i), acc);
+    if (k < ng) {
+      G q[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[k + j], at, k + j < ng);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t dead = k + j < ng ? 0u : 0x80008000u;   // both halves -0.0
+        accumulate(G{q[j].x | dead, q[j].y | dead}, acc);
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < SV; ++e) acc[e] = acc[e] * gs;
@@ -299,20 +333,20 @@ __device__ __forceinline__ void add_row(u32x2 q, float (&x)[4]) {
 // rows of a group are loaded before they are added.
 template <int SV, bool BACC>
 __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, int ng, int group,
-                                                    float gs, int64_t i, float (&acc)[SV]) {
+                                                    float gs, At at, float (&acc)[SV]) {
   using G = u32x2;
   for (int base = 0; base < ng; base += group) {
     float part[SV];
-    unpack(ldh<G, kGradNt>(g[base] + i), part);
+    unpack(ld_tile<G, kGradNt>(g[base], at), part);
     int k = 1;
     for (; k + 8 <= group; k += 8) {
       G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ldh<G, kGradNt>(g[base + k + j] + i);
+      for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[base + k + j], at);
 #pragma unroll
       for (int j = 0; j < 8; ++j) add_row<BACC>(q[j], part);
     }
-    for (; k < group; ++k) add_row<BACC>(ldh<G, kGradNt>(g[base + k] + i), part);
+    for (; k < group; ++k) add_row<BACC>(ld_tile<G, kGradNt>(g[base + k], at), part);
     if (base == 0) {
 #pragma unroll
       for (int e = 0; e < SV; ++e) acc[e] = part[e];
@@ -330,12 +364,13 @@ __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, in
 // all NG row loads issued before the first add. Same operations in the same
 // order as reduce_rows_general.
 template <int NG, int GRP, bool BACC>
-__device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, float gs, int64_t i,
+__device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, float gs, At at,
                                                     float (&acc)[4]) {
   static_assert(NG % GRP == 0, "whole groups");
   u32x2 q[NG];
 #pragma unroll
-  for (int k = 0; k < NG; ++k) q[k] = ldh<u32x2, kGradNt>(g[k] + i);
+  for (int k = 0; k < NG; ++k) q[k] = ld_tile<u32x2, kGradNt>(g[k], at);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < NG; b += GRP) {
     float part[4];
@@ -460,31 +495,36 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
     const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
     if (i >= n) continue;
     if (i + kSV <= n) {
-      float g[kSV];
+      const int64_t tl = n - t0 < tile ? n - t0 : tile;
+      const At at{t0, tl, uint32_t(threadIdx.x) * kSV};
+      float g[kSV], p[kSV], m[kSV], v[kSV];
+      // The state loads go first: with a compile-time row count every load of
+      // the tile is then in flight before the first add, and the run-time fold
+      // overlaps them with its first chunks.
+      if constexpr (OP != Op::Reduce) {
+        loadf(a.p, at, p);
+        loadf(a.m, at, m);
+        loadf(a.v, at, v);
+      }
       if constexpr (OP == Op::AdamW) {
-        loadf<kSV>(a.grad + i, g);
+        loadf(a.grad, at, g);
       } else {
         if constexpr (NG == 0) {
           if (a.bf16acc)
-            reduce_rows_general<kSV, true>(a.g, a.n_grads, a.group, a.s.gs, i, g);
+            reduce_rows_general<kSV, true>(a.g, a.n_grads, a.group, a.s.gs, at, g);
           else if (a.group < a.n_grads)
-            reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, i, g);
+            reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, at, g);
           else
-            reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+            reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, at, g);
         } else if constexpr (GRP > 0) {
-          reduce_rows_grouped<NG, GRP, BACC>(a.g, a.s.gs, i, g);
+          reduce_rows_grouped<NG, GRP, BACC>(a.g, a.s.gs, at, g);
         } else {
-          reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, i, g);
+          reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, at, g);
         }
       }
-      const int64_t tl = n - t0 < tile ? n - t0 : tile;
       if constexpr (OP == Op::Reduce) {
         out_f32(a.out, t0, tl, i, g);
       } else {
-        float p[kSV], m[kSV], v[kSV];
-        loadf<kSV>(a.p + i, p);
-        loadf<kSV>(a.m + i, m);
-        loadf<kSV>(a.v + i, v);
 #pragma unroll
         for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
         out_f32(a.p, t0, tl, i, p);
@@ -520,9 +560,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
         out_f32(a.out, t0, tl, i, g);
       } else {
         float p[V], m[V], v[V];
-        loadf<V>(a.p + i, p);
-        loadf<V>(a.m + i, m);
-        loadf<V>(a.v + i, v);
+        const At at{t0, tl, uint32_t(threadIdx.x) * V};
+        loadf(a.p, at, p);
+        loadf(a.m, at, m);
+        loadf(a.v, at, v);
 #pragma unroll
         for (int e = 0; e < V; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
         out_f32(a.p, t0, tl, i, p);
@@ -609,11 +650,12 @@ __global__ __launch_bounds__(kStepThreads) void k_step_multi(MultiArgs a) {
     const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
     if (i + kSV <= d.n) {
       const int64_t tl = d.n - t0 < kStepTile ? d.n - t0 : int64_t(kStepTile);
+      const At at{t0, tl, uint32_t(threadIdx.x) * kSV};
       float g[kSV], p[kSV], m[kSV], v[kSV];
-      reduce_rows<NG, kSV>(d.g, a.n_grads, a.s.gs, i, g);
-      loadf<kSV>(d.p + i, p);
-      loadf<kSV>(d.m + i, m);
-      loadf<kSV>(d.v + i, v);
+      loadf(d.p, at, p);            // state first: every load in flight before the first add
+      loadf(d.m, at, m);
+      loadf(d.v, at, v);
+      reduce_rows<NG, kSV>(d.g, a.n_grads, a.s.gs, at, g);
 #pragma unroll
       for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
       out_f32(d.p, t0, tl, i, p);
@@ -799,9 +841,10 @@ size_t lds_reservation(int wg_per_cu) {
 // buffers, several boxes and allocations):
 //  * launches under 2^FSDP_CAP_MIN_LOG2 elements run 256-thread workgroups, all
 //    resident at once: they have fewer tiles than a few rounds of the machine;
-//  * the reduce, the stand-alone AdamW and the fused kernels with a
-//    compile-time flat fold run one-wave workgroups (64 threads, 256-element
-//    tiles), with the per-CU count set so that a CU keeps about
+//  * the stand-alone AdamW and the reduce and fused kernels with a
+//    compile-time fold (flat, or grouped for hybrid sharding and bf16 partial
+//    sums) run one-wave workgroups (64 threads, 256-element tiles), with the
+//    per-CU count set so that a CU keeps about
 //    FSDP_LANE_BUDGET * 64 bytes of loads and stores in flight: count =
 //    round(FSDP_LANE_BUDGET / bytes a lane moves per tile), within [8, 32]. A
 //    lane moves 8 bytes per gradient row and 16 bytes per fp32 array, read or
@@ -811,12 +854,12 @@ size_t lds_reservation(int wg_per_cu) {
 //    size: a CU's 1/256 share of 8 TB/s over a loaded latency of a few
 //    microseconds. The one-wave tiles keep each CU's write streams short and
 //    the end of a launch short;
-//  * the compile-time grouped folds (hybrid sharding, bf16 partial sums), which
-//    measured no faster in that shape, run 256-thread workgroups, at most
-//    FSDP_FUSED_WG_PER_CU per CU (12 waves) when fused, or 128-thread ones at
-//    2^FSDP_HALF_TILE_MIN_LOG2+ elements with the count doubled;
-//  * the fused kernels that walk a run-time row count in dependent chunks are
-//    never capped (256 threads).
+//  * the folds of a run-time row count (flat or grouped) are never capped
+//    (256 threads). One-wave workgroups at 8 to 24 per CU, with one or two
+//    chunks of rows in flight per lane, ran up to 10% faster on some row
+//    layouts and ranks (11, 13 and 64 rows) and up to 15% slower on others
+//    (the last rank's windows in one large allocation per row); on average
+//    they were no faster, so the shape that varies least stays.
 struct Shape {
   int threads;
   int wg_per_cu;
@@ -843,16 +886,12 @@ int lane_bytes(const StepArgs& a) {
 template <Op OP>
 Shape step_shape(const StepArgs& a) {
   if (a.n < (int64_t(1) << FSDP_CAP_MIN_LOG2)) return Shape{kStepThreads, 0};
-  const bool flat = a.group == a.n_grads && !a.bf16acc;
-  if (OP == Op::AdamW || (flat && compile_time_fold(a))) {
+  if (OP == Op::AdamW || compile_time_fold(a)) {
     const int b = lane_bytes<OP>(a);
     const int wg = std::min(32, std::max(8, (FSDP_LANE_BUDGET + b / 2) / b));
     return Shape{kSmallThreads, wg};
   }
-  if (!compile_time_fold(a)) return Shape{kStepThreads, 0};
-  const int base = OP == Op::Reduce ? 0 : FSDP_FUSED_WG_PER_CU;   // reduce-only: uncapped
-  if (a.n >= (int64_t(1) << FSDP_HALF_TILE_MIN_LOG2)) return Shape{kStepThreads / 2, 2 * base};
-  return Shape{kStepThreads, base};
+  return Shape{kStepThreads, 0};   // a run-time row count
 }
 
 template <Op OP, bool EMIT>

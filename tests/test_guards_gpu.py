@@ -149,21 +149,40 @@ def test_grouped_fold_guards(lib, kind):
         t.check(f"{kind} {nm}")
 
 
-@pytest.mark.parametrize("rank", [0, 1], ids=["vector_rows", "shifted_rows"])
-def test_long_launch_guards(lib, rank):
-    """The one-wave-workgroup shape (8 rows, 2^24 + 3 elements: a ragged last tile),
-    with aligned gradient windows (rank 0) and windows at a 6-byte offset (rank 1: the
-    shifted-row path): the guards around the windows and the elements at both ends."""
-    F, S = 8, (1 << 24) + 3
+LONG_GUARD_CASES = [
+    # name, F, S, rank: 8 rows over 2^24 + 3 elements (a ragged last tile) in one-wave
+    # workgroups, with aligned gradient windows (rank 0) and windows at a 6-byte offset
+    # (rank 1: the shifted-row path); 11 and 64 rows folded in chunks of 8 at run time
+    # (the 11-row fold ends in a partial chunk), over 2^23 + 5 and 2^22 + 7 elements
+    ("vector_rows", 8, (1 << 24) + 3, 0),
+    ("shifted_rows", 8, (1 << 24) + 3, 1),
+    ("chunked_rows11", 11, (1 << 23) + 5, 0),
+    ("chunked_rows64", 64, (1 << 22) + 7, 0),
+]
+
+
+@pytest.mark.parametrize("name,F,S,rank", LONG_GUARD_CASES, ids=[c[0] for c in LONG_GUARD_CASES])
+def test_long_launch_guards(lib, name, F, S, rank):
+    """Long launches, fused and reduce: the guards around the windows and the
+    elements at both ends. Row k is the U-element view of one arena that starts at
+    element k*S (disjoint rank windows)."""
     u = lib.Unit([(F * S,)], F, rank)
     n = u.shard_valid
-    assert n == S and ((2 * u.shard_begin) % 8 == 0) == (rank == 0)
-    rows = rows_for(u, F)
+    assert n == S and ((2 * u.shard_begin) % 8 == 0) == (name != "shifted_rows")
+    arena = torch.zeros((F - 1) * S + u.U, dtype=torch.bfloat16, device="cuda")
+    rows = []
+    for k in range(F):
+        r = arena[k * S:k * S + u.U]
+        datagen.fill_bf16_(r[u.shard_begin:u.shard_begin + n], 5, k, 1e-3, start=u.shard_begin)
+        rows.append(r)
     p, m, v = state_for(n)
     w = Guarded(n, torch.bfloat16)
     lib.reduce_adamw_shard(u, rows, p.win, m.win, v.win, w.win, hp(lib), 1)
+    out = Guarded(n, torch.float32)
+    lib.reduce_shard(u, rows, out.win)
     torch.cuda.synchronize()
-    for t, nm in ((p, "master"), (m, "exp_avg"), (v, "exp_avg_sq"), (w, "bf16 parameter")):
+    for t, nm in ((p, "master"), (m, "exp_avg"), (v, "exp_avg_sq"), (w, "bf16 parameter"),
+                  (out, "reduce out")):
         b = t.bits
         assert (b[:t.lead].cpu().numpy() == t.sentinel).all(), f"{nm}: guard before"
         assert (b[t.lead + n:].cpu().numpy() == t.sentinel).all(), f"{nm}: guard after"

@@ -696,12 +696,14 @@ def test_bf16acc_blk7_sampled():
         assert_bits(_bits(gather(got, loc)), _bits(exp), f"bf16acc blk7 {name}")
 
 
-def test_unfused_long_launch_sampled():
+@pytest.mark.parametrize("n_grads", [8, 11, 24])
+def test_unfused_long_launch_sampled(n_grads):
     """fsdp_reduce_shard then fsdp_adamw_shard on a 202,383,360-element shard (the 7B
-    block at F=1, 8 gradient rows): the one-wave workgroups of long launches, 16 per CU
-    for this reduce and 11 for the AdamW; sampled indices against the oracle, two
-    steps."""
-    case = Case(W.shapes(W.BLK7), 1, 0, n_grads=8, config=44)
+    block at F=1): 8 gradient rows (a compile-time fold in one-wave workgroups, 16
+    per CU for this reduce, 11 for the AdamW), 11 and 24 rows (a run-time count
+    folded in chunks of 8; the 11-row fold ends in a partial chunk); sampled indices
+    against the oracle, two steps."""
+    case = Case(W.shapes(W.BLK7), 1, 0, n_grads=n_grads, config=44)
     u = fsdp.Unit(case.shapes, 1, 0)
     assert u.shard_valid >= 1 << 25
     p = torch.empty(u.S, dtype=torch.float32, device=DEV)
@@ -718,7 +720,7 @@ def test_unfused_long_launch_sampled():
     loc = case.sample_indices()
     want = case.oracle_sampled(loc, 2)[-1]
     for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
-        assert_bits(_bits(gather(got, loc)), _bits(exp), f"unfused F=1 {name}")
+        assert_bits(_bits(gather(got, loc)), _bits(exp), f"unfused F=1 {n_grads} rows {name}")
 
 
 def test_sharded_steps_concatenated_equal_the_ddp_step():

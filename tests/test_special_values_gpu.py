@@ -12,10 +12,14 @@ the oracle: bit-equal, or NaN on both sides.
 
 Paths covered: the vector path (aligned windows, with and without a ragged
 tail), the shifted-row path (a rank window r*S with S odd), the scalar path
-(fp32 state not 16-byte aligned), the one-wave-workgroup shape of long fused
-launches (a 25M-element shard, sampled), the compile-time grouped folds
-(hybrid sharding, bf16 partial sums) and a run-time row count; entry points:
-fused with and without the bf16 emission, and the unfused reduce + AdamW pair.
+(fp32 state not 16-byte aligned), long fused launches (a 25M-element shard
+with 8 rows in one-wave workgroups, and 11 and 64 rows folded in chunks of 8
+at run time; sampled), the compile-time grouped folds (hybrid
+sharding, bf16 partial sums) and a run-time row count; entry points: fused
+with and without the bf16 emission, and the unfused reduce + AdamW pair. The
+run-time fold starts from -0.0 rather than from rank 0's value; -0.0 is the
+exact identity of IEEE addition, so the sums are the same, and the planted
+-0.0 rows check that.
 """
 
 import zlib
@@ -261,23 +265,37 @@ def test_unfused_special_values(lib, case):
 # a full-size launch: the one-wave-workgroup shape of long fused launches
 # ---------------------------------------------------------------------------
 
-def test_fused_special_values_long_launch(lib):
-    """8 rows over a 25,297,920-element shard (rank 3 of F=8): normal draws in HBM
-    with specials planted at 2^17 random positions and in one contiguous run
-    that spans several workgroup tiles; those positions and the run are
-    compared with the oracle element by element."""
-    F, S, rank, n_rows = 8, 25297920, 3, 8
+LONG_CASES = [
+    # F, S, rank: 8 rows over the 7B block's shard at F = 8 (compile-time fold, one-wave
+    # workgroups); 11 rows and 64 rows, folded in chunks of 8 at run time (for 11 rows
+    # the last chunk is partial)
+    (8, 25297920, 3),
+    (11, (1 << 23) + 5, 4),
+    (64, (1 << 22) + 7, 5),
+]
+
+
+@pytest.mark.parametrize("F,S,rank", LONG_CASES, ids=[f"rows{c[0]}" for c in LONG_CASES])
+def test_fused_special_values_long_launch(lib, F, S, rank):
+    """F rows over an S-element shard (rank `rank` of F): normal draws in HBM with
+    specials planted at 2^17 random positions and in one contiguous run that spans
+    several workgroup tiles; those positions and the run are compared with the
+    oracle element by element. Row k is the U-element view of one arena that
+    starts at element k*S, so the rank windows of the rows are disjoint (the views
+    overlap outside them, where the step reads nothing)."""
+    n_rows = F
     shapes = [(F * S,)]
     L = O.unit_layout(shapes, F, rank)
     u = lib.Unit(shapes, F, rank)
     n = L.shard_valid
-    rng = np.random.default_rng(11)
+    rng = np.random.default_rng(11 + F)
     run = np.arange(123456, 123456 + 3000, dtype=np.int64)
     pos = np.unique(np.concatenate([rng.integers(0, n, 1 << 17), run, [0, n - 1]]))
     gseed, mseed = datagen.seed_for(9, 1, 77), datagen.seed_for(9, 0, 77)
+    arena = torch.empty((n_rows - 1) * S + L.U, dtype=torch.bfloat16, device="cuda")
     rows_dev, rows_at = [], []
     for k in range(n_rows):
-        r = torch.empty(L.U, dtype=torch.bfloat16, device="cuda")
+        r = arena[k * S:k * S + L.U]          # window: arena[kS + begin, kS + begin + S)
         datagen.fill_bf16_(r[L.shard_begin:L.shard_begin + n], gseed, k, 1e-3,
                            start=L.shard_begin)
         at = datagen.bf16_bits_host(gseed, k, L.shard_begin + pos, 1e-3)
