@@ -433,6 +433,10 @@ __device__ __forceinline__ u32x2 ld_row_shifted(const uint16_t* p) {
   return u32x2{uint32_t(v), uint32_t(v >> 32)};
 }
 
+// Left fold of the shifted rows for the 4 elements at i, times gs. NG > 0:
+// the compile-time count, every load issued before the first add. NG == 0:
+// chunks of 8 rows from -0.0, as in reduce_rows (rows past the count are not
+// read and add -0.0).
 template <int NG>
 __device__ __forceinline__ void reduce_rows_shifted(const StepArgs& a, int64_t i,
                                                     float (&acc)[4]) {
@@ -440,21 +444,23 @@ __device__ __forceinline__ void reduce_rows_shifted(const StepArgs& a, int64_t i
     u32x2 q[NG];
 #pragma unroll
     for (int k = 0; k < NG; ++k) q[k] = ld_row_shifted(a.g[k] + i);
+    __builtin_amdgcn_sched_barrier(0);
     unpack(q[0], acc);
 #pragma unroll
     for (int k = 1; k < NG; ++k) accumulate(q[k], acc);
   } else {
+    static_assert(FSDP_MAX_RANKS % 8 == 0, "whole chunks of row pointers");
     const int ng = a.n_grads;
-    unpack(ld_row_shifted(a.g[0] + i), acc);
-    int k = 1;
-    for (; k + 8 <= ng; k += 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = -0.0f;
+    for (int k = 0; k < ng; k += 8) {   // k + 7 < FSDP_MAX_RANKS: k is a multiple of 8 below ng
       u32x2 q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ld_row_shifted(a.g[k + j] + i);
+      for (int j = 0; j < 8; ++j)
+        q[j] = k + j < ng ? ld_row_shifted(a.g[k + j] + i) : u32x2{0x80008000u, 0x80008000u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) accumulate(q[j], acc);
     }
-    for (; k < ng; ++k) accumulate(ld_row_shifted(a.g[k] + i), acc);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = acc[e] * a.s.gs;
@@ -538,10 +544,25 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   }
 }
 
+// Tile of workgroup b on the shifted-row path: runs of kShiftRun consecutive
+// tiles on one XCD (workgroup b runs on XCD b % 8). Misaligned rows put each
+// tile's first and last 128-byte line of every row in two tiles; tiles that
+// share a line then share an L2, and the line is read from HBM once instead of
+// once per XCD (with consecutive tiles on different XCDs the rows cost a
+// quarter more HBM reads; with runs of 8, 1/32 more). The workgroups past the
+// last whole group of 8 runs keep their own index.
+constexpr unsigned kShiftRun = 8;
+__device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
+  const unsigned whole = nb / (8 * kShiftRun) * (8 * kShiftRun);
+  if (b >= whole) return b;
+  const unsigned j = b / 8;
+  return int64_t(j / kShiftRun) * (8 * kShiftRun) + (b % 8) * kShiftRun + j % kShiftRun;
+}
+
 // Shifted-row path: fp32 state (and the bf16 output) aligned, gradient rows
-// only 2-byte aligned (a rank window r*S with r*S not a multiple of 4). Same
-// lane layout as the vector path with kSV = 4; the first group and the last
-// 8 elements go through the scalar step.
+// only 2-byte aligned (a rank window r*S with r*S not a multiple of 4). The
+// lane layout and tiles of the vector path, the tiles visited in XCD runs; the
+// first group and the last 8 elements go through the scalar step.
 template <Op OP, int NG, bool EMIT>
 __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   static_assert(OP != Op::AdamW, "only the gradient rows are shifted");
@@ -549,21 +570,22 @@ __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   const int64_t TILE = int64_t(blockDim.x) * V;          // 64, 128 or 256 threads
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * TILE;
-  for (int64_t t0 = int64_t(blockIdx.x) * TILE; t0 < n; t0 += stride) {
+  for (int64_t t0 = shift_tile(blockIdx.x, gridDim.x) * TILE; t0 < n; t0 += stride) {
     const int64_t i = t0 + int64_t(threadIdx.x) * V;     // t0 is workgroup-uniform
     if (i >= n) continue;
     if (i >= V && i + 2 * V <= n) {
-      float g[V];
-      reduce_rows_shifted<NG>(a, i, g);
+      float g[V], p[V], m[V], v[V];
       const int64_t tl = n - t0 < TILE ? n - t0 : TILE;
-      if constexpr (OP == Op::Reduce) {
-        out_f32(a.out, t0, tl, i, g);
-      } else {
-        float p[V], m[V], v[V];
-        const At at{t0, tl, uint32_t(threadIdx.x) * V};
+      const At at{t0, tl, uint32_t(threadIdx.x) * V};
+      if constexpr (OP != Op::Reduce) {   // the state loads first, as on the vector path
         loadf(a.p, at, p);
         loadf(a.m, at, m);
         loadf(a.v, at, v);
+      }
+      reduce_rows_shifted<NG>(a, i, g);
+      if constexpr (OP == Op::Reduce) {
+        out_f32(a.out, t0, tl, i, g);
+      } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
         out_f32(a.p, t0, tl, i, p);

@@ -556,16 +556,22 @@ def test_blk7_f8_sampled_bit_equal(blk7_grads):
 # gradient rows whose window is not 8-byte aligned (shifted-row vector path)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shift", [1, 2, 3])
+@pytest.mark.parametrize("shift", [1, 2, 3, "mixed"])
 @pytest.mark.parametrize("ng", [8, 9])
 @pytest.mark.parametrize("fused", [True, False])
 def test_shifted_rows_with_aligned_state(shift, ng, fused):
+    """Rank 1 of F=4 with S = 5283 (odd): the rank window starts 6 bytes past an 8-byte
+    boundary, and each row is further offset by `shift` elements ("mixed": row k by
+    k mod 4, so the rows' windows sit at all four 2-byte offsets from 8-byte
+    boundaries). 21 full 252-element runs and a ragged end; 8 rows (compile-time fold)
+    and 9 (run-time fold ending in a partial chunk)."""
     shapes = [(3000, 7), (129,)]
     F, rank = 4, 1
     case = Case(shapes, F, rank, n_grads=ng, config=10)
     u = fsdp.Unit(shapes, F, rank)
     big = [torch.empty(u.U + 8, dtype=torch.bfloat16, device=DEV) for _ in range(ng)]
-    grads = [b[shift:shift + u.U] for b in big]      # 2*shift bytes past a 512-byte boundary
+    offs = [k % 4 if shift == "mixed" else shift for k in range(ng)]
+    grads = [b[o:o + u.U] for b, o in zip(big, offs)]   # 2*o bytes past a 512-byte boundary
     case.device_grads(1, out=grads)
     flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], F)
     n = u.shard_valid
