@@ -257,7 +257,7 @@ struct StepArgs {
   int32_t n_grads;
   int32_t group;                      // rows per replica group (== n_grads: one flat fold)
   int32_t bf16acc;                    // 1: every partial sum rounded to bf16
-  int32_t pad_;
+  int32_t runs;                       // 1: tiles visited in XCD runs (shift_tile)
   Adam s;
 };
 
@@ -486,6 +486,24 @@ __device__ __forceinline__ void step_scalar(const StepArgs& a, int64_t i) {
   }
 }
 
+// Tile of workgroup b when the tiles are visited in XCD runs: runs of kShiftRun
+// consecutive tiles on one XCD (workgroup b runs on XCD b % 8). When an array's
+// window does not start on a 128-byte line (every misaligned gradient row, and
+// any array placed off a line boundary), each tile's first and last line of it
+// also belong to the neighbouring tiles; tiles that share a line then share an
+// L2, and the line moves between HBM and L2 once instead of once per XCD (with
+// consecutive tiles on different XCDs, misaligned rows cost up to a quarter
+// more HBM reads). The workgroups past the last whole group of 8 runs keep
+// their own index. With every window on a line boundary the plain order is
+// kept: the runs measured no faster there.
+constexpr unsigned kShiftRun = 8;
+__device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
+  const unsigned whole = nb / (8 * kShiftRun) * (8 * kShiftRun);
+  if (b >= whole) return b;
+  const unsigned j = b / 8;
+  return int64_t(j / kShiftRun) * (8 * kShiftRun) + (b % 8) * kShiftRun + j % kShiftRun;
+}
+
 // Vector path: bf16 rows aligned to 2*kSV bytes, fp32 buffers to 16 bytes.
 // Lane t of a tile owns elements [tile + kSV*t, tile + kSV*t + kSV), so every
 // load and store instruction of a wavefront covers one contiguous range; the
@@ -495,7 +513,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
   const int64_t tile = int64_t(blockDim.x) * kSV;          // 64, 128 or 256 threads per workgroup
   const int64_t stride = int64_t(gridDim.x) * tile;
-  for (int64_t t0 = int64_t(blockIdx.x) * tile; t0 < n; t0 += stride) {
+  const int64_t first = a.runs ? shift_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
+  for (int64_t t0 = first * tile; t0 < n; t0 += stride) {
     // t0, this tile's first element, is workgroup-uniform (the store descriptors
     // are built from it in scalar registers)
     const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
@@ -544,25 +563,10 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   }
 }
 
-// Tile of workgroup b on the shifted-row path: runs of kShiftRun consecutive
-// tiles on one XCD (workgroup b runs on XCD b % 8). Misaligned rows put each
-// tile's first and last 128-byte line of every row in two tiles; tiles that
-// share a line then share an L2, and the line is read from HBM once instead of
-// once per XCD (with consecutive tiles on different XCDs the rows cost a
-// quarter more HBM reads; with runs of 8, 1/32 more). The workgroups past the
-// last whole group of 8 runs keep their own index.
-constexpr unsigned kShiftRun = 8;
-__device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
-  const unsigned whole = nb / (8 * kShiftRun) * (8 * kShiftRun);
-  if (b >= whole) return b;
-  const unsigned j = b / 8;
-  return int64_t(j / kShiftRun) * (8 * kShiftRun) + (b % 8) * kShiftRun + j % kShiftRun;
-}
-
 // Shifted-row path: fp32 state (and the bf16 output) aligned, gradient rows
 // only 2-byte aligned (a rank window r*S with r*S not a multiple of 4). The
-// lane layout and tiles of the vector path, the tiles visited in XCD runs; the
-// first group and the last 8 elements go through the scalar step.
+// lane layout and tiles of the vector path, the tiles always visited in XCD
+// runs; the first group and the last 8 elements go through the scalar step.
 template <Op OP, int NG, bool EMIT>
 __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   static_assert(OP != Op::AdamW, "only the gradient rows are shifted");
@@ -972,9 +976,23 @@ void launch_shift_ng(const StepArgs& a, unsigned grid, int threads, size_t lds,
 
 enum class Path { Vector, Shifted, Scalar };
 
+// Whether a vector-path launch visits its tiles in XCD runs: some window it
+// reads or writes does not start on a 128-byte line.
+bool off_line(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 127u); }
+bool needs_runs(const StepArgs& a, Op op) {
+  bool r = false;
+  if (op != Op::AdamW)
+    for (int k = 0; k < a.n_grads; ++k) r = r || off_line(a.g[k]);
+  if (op == Op::AdamW) r = r || off_line(a.grad);
+  if (op == Op::Reduce) return r || off_line(a.out);
+  return r || off_line(a.p) || off_line(a.m) || off_line(a.v) || off_line(a.w);
+}
+
 template <Op OP>
-fsdp_status launch_step(const StepArgs& a, Path path, hipStream_t stream, const char* what) {
-  if (a.n <= 0) return FSDP_OK;
+fsdp_status launch_step(const StepArgs& args, Path path, hipStream_t stream, const char* what) {
+  if (args.n <= 0) return FSDP_OK;
+  StepArgs a = args;
+  a.runs = needs_runs(a, OP) ? 1 : 0;
   if (path == Path::Vector) {
     const Shape sh = step_shape<OP>(a);
     const int64_t tile = int64_t(sh.threads) * kSV;
