@@ -94,6 +94,11 @@
 #ifndef FSDP_LANE_BUDGET
 #define FSDP_LANE_BUDGET 1280
 #endif
+// One-wave workgroups per CU for the fused step with a run-time row count
+// (folded flat in chunks of 8 rows) on 2^FSDP_CAP_MIN_LOG2+ elements.
+#ifndef FSDP_CHUNKED_WG_PER_CU
+#define FSDP_CHUNKED_WG_PER_CU 12
+#endif
 
 using fsdp::fail;
 
@@ -880,12 +885,14 @@ size_t lds_reservation(int wg_per_cu) {
 //    size: a CU's 1/256 share of 8 TB/s over a loaded latency of a few
 //    microseconds. The one-wave tiles keep each CU's write streams short and
 //    the end of a launch short;
-//  * the folds of a run-time row count (flat or grouped) are never capped
-//    (256 threads). One-wave workgroups at 8 to 24 per CU, with one or two
-//    chunks of rows in flight per lane, ran up to 10% faster on some row
-//    layouts and ranks (11, 13 and 64 rows) and up to 15% slower on others
-//    (the last rank's windows in one large allocation per row); on average
-//    they were no faster, so the shape that varies least stays.
+//  * the fused step with a run-time row count, folded flat, runs one-wave
+//    workgroups, FSDP_CHUNKED_WG_PER_CU per CU: a lane has one chunk of 8 rows
+//    in flight at a time, so it needs more waves than its bytes suggest (11
+//    and 13 rows: best at 12 out of 6 to 24; 2-7% faster than 256-thread
+//    workgroups at rank 0, -1 to +3% at the last rank);
+//  * the reduce with a run-time row count, and the grouped folds of a
+//    run-time count, are not capped (256 threads): one-wave workgroups made
+//    that reduce 3-20% slower.
 struct Shape {
   int threads;
   int wg_per_cu;
@@ -917,7 +924,9 @@ Shape step_shape(const StepArgs& a) {
     const int wg = std::min(32, std::max(8, (FSDP_LANE_BUDGET + b / 2) / b));
     return Shape{kSmallThreads, wg};
   }
-  return Shape{kStepThreads, 0};   // a run-time row count
+  if (OP == Op::Fused && a.group == a.n_grads && !a.bf16acc)
+    return Shape{kSmallThreads, FSDP_CHUNKED_WG_PER_CU};   // a run-time count, folded flat
+  return Shape{kStepThreads, 0};   // a run-time row count: the reduce, the grouped folds
 }
 
 template <Op OP, bool EMIT>
