@@ -595,6 +595,52 @@ def test_shifted_rows_with_aligned_state(shift, ng, fused):
 
 
 # ---------------------------------------------------------------------------
+# tiles visited in XCD runs: every element of a long launch, ragged
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("offset", [12, 1], ids=["rows_off_line", "rows_shifted"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_xcd_runs_cover_every_element(offset, fused):
+    """3 gradient rows whose windows start `offset` elements past a 128-byte line (12:
+    8-byte aligned, the vector path; 1: 2 bytes off, the shifted path), over
+    2^23 + 12345 elements: both paths visit their tiles in runs of 8 per XCD. The launch
+    has 32,817 one-wave tiles: 512 whole groups of 64 (8 runs of 8) and 49 tiles past them
+    in the plain order, the last one ragged. Every element against the oracle, bit for
+    bit."""
+    n = (1 << 23) + 12345
+    shapes, F, rank, ng = [(n,)], 1, 0, 3
+    u = fsdp.Unit(shapes, F, rank)
+    L = O.unit_layout(shapes, F, rank)
+    seed = datagen.seed_for(46, 1, 1)
+    bufs = [torch.empty(n + 64, dtype=torch.bfloat16, device=DEV) for _ in range(ng)]
+    rows = [b[offset:offset + n] for b in bufs]
+    for k, r in enumerate(rows):
+        datagen.fill_bf16_(r, seed, k, W.GRAD_SIGMA)
+    host = [to_np(r) for r in rows]
+    if not fused:
+        out = torch.empty(n, dtype=torch.float32, device=DEV)
+        fsdp.reduce_shard(u, rows, out)
+        torch.cuda.synchronize()
+        assert_bits(to_np(out).view(np.uint32), O.reduce_shard(host, L).view(np.uint32),
+                    f"reduce, rows {offset} elements off a line")
+        return
+    p = torch.empty(n, dtype=torch.float32, device=DEV)
+    datagen.fill_normal_f32_(p, datagen.seed_for(46, 0), 0, W.MASTER_SIGMA)
+    m = torch.empty(n, dtype=torch.float32, device=DEV)
+    datagen.fill_normal_f32_(m, datagen.seed_for(46, 0), 1, 1e-4)
+    v = torch.empty(n, dtype=torch.float32, device=DEV)
+    datagen.fill_normal_f32_(v, datagen.seed_for(46, 0), 2, 1e-6)
+    v.abs_()
+    p0, m0, v0 = to_np(p).copy(), to_np(m).copy(), to_np(v).copy()
+    w = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    fsdp.reduce_adamw_shard(u, rows, p, m, v, w, HPD, 3)
+    torch.cuda.synchronize()
+    want = O.reduce_adamw_shard(host, L, p0, m0, v0, HP, 3, emit_bf16=True)
+    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+        assert_bits(_bits(to_np(got)), _bits(exp), f"fused {name}, rows {offset} elements off a line")
+
+
+# ---------------------------------------------------------------------------
 # hybrid sharding (HSDP): R replica groups of F ranks
 # ---------------------------------------------------------------------------
 
