@@ -54,7 +54,7 @@
 #pragma clang fp contract(off)
 
 #ifndef FSDP_COPY_BLOCK
-#define FSDP_COPY_BLOCK 256   // threads per workgroup, copy kernels
+#define FSDP_COPY_BLOCK 64    // threads per workgroup, copy kernels (one wave)
 #endif
 #ifndef FSDP_STEP_BLOCK
 #define FSDP_STEP_BLOCK 256   // threads per workgroup, reduce/AdamW kernels
