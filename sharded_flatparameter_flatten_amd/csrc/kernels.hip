@@ -57,7 +57,7 @@
 #define FSDP_COPY_BLOCK 64    // threads per workgroup, copy kernels (one wave)
 #endif
 #ifndef FSDP_STEP_BLOCK
-#define FSDP_STEP_BLOCK 256   // threads per workgroup, reduce/AdamW kernels
+#define FSDP_STEP_BLOCK 256   // threads per workgroup of the step launches not in one-wave shape
 #endif
 #ifndef FSDP_GRAD_NT_LOAD
 #define FSDP_GRAD_NT_LOAD 1   // streaming hint on the gradient-row loads (read once)
@@ -516,7 +516,7 @@ __device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
 template <Op OP, int NG, bool EMIT, int GRP = 0, bool BACC = false>
 __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
   const int64_t n = a.n;
-  const int64_t tile = int64_t(blockDim.x) * kSV;          // 64, 128 or 256 threads per workgroup
+  const int64_t tile = int64_t(blockDim.x) * kSV;          // 64 or 256 threads per workgroup
   const int64_t stride = int64_t(gridDim.x) * tile;
   const int64_t first = a.runs ? shift_tile(blockIdx.x, gridDim.x) : int64_t(blockIdx.x);
   for (int64_t t0 = first * tile; t0 < n; t0 += stride) {
@@ -576,7 +576,7 @@ template <Op OP, int NG, bool EMIT>
 __global__ __launch_bounds__(kStepThreads) void k_step_shift(StepArgs a) {
   static_assert(OP != Op::AdamW, "only the gradient rows are shifted");
   constexpr int V = 4;
-  const int64_t TILE = int64_t(blockDim.x) * V;          // 64, 128 or 256 threads
+  const int64_t TILE = int64_t(blockDim.x) * V;          // 64 or 256 threads
   const int64_t n = a.n;
   const int64_t stride = int64_t(gridDim.x) * TILE;
   for (int64_t t0 = shift_tile(blockIdx.x, gridDim.x) * TILE; t0 < n; t0 += stride) {
