@@ -251,7 +251,9 @@ __device__ __forceinline__ void out_bf16(uint16_t* base, int64_t t0, int64_t len
 // ---------------------------------------------------------------------------
 
 struct StepArgs {
-  const uint16_t* g[FSDP_MAX_RANKS];  // rank-window start of each contribution
+  // rank-window start of each contribution; 8 more null entries, so that a
+  // chunk of 8 row pointers starting below n_grads stays inside the array
+  const uint16_t* g[FSDP_MAX_RANKS + 8];
   const float* grad;                  // AdamW input (unfused)
   float* out;                         // reduce output (unfused)
   float* p;
@@ -334,8 +336,12 @@ __device__ __forceinline__ void add_row(u32x2 q, float (&x)[4]) {
 // [rho*group, (rho+1)*group) are one replica group: each group is folded on
 // its own (the reduce-scatter inside the group), then the group sums are
 // folded in group order (the all-reduce across groups), then scaled. With
-// BACC every addition is an fp32 add followed by rounding to bf16. Up to 8
-// rows of a group are loaded before they are added.
+// BACC every addition is an fp32 add followed by rounding to bf16. A group's
+// first row starts its partial sum; the rest follow in chunks of 8, each
+// chunk's loads issued before its first add; in the last, partial chunk the
+// rows past the group load nothing and add -0.0, which changes no sum (the
+// partial is already a bf16 value when BACC, and -0.0 is the exact identity
+// of the add; a NaN partial is already quiet from the chunk's live rows).
 template <int SV, bool BACC>
 __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, int ng, int group,
                                                     float gs, At at, float (&acc)[SV]) {
@@ -343,15 +349,16 @@ __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, in
   for (int base = 0; base < ng; base += group) {
     float part[SV];
     unpack(ld_tile<G, kGradNt>(g[base], at), part);
-    int k = 1;
-    for (; k + 8 <= group; k += 8) {
+    for (int k = 1; k < group; k += 8) {   // g[base + k + 7]: inside the padded array
       G q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[base + k + j], at);
+      for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[base + k + j], at, k + j < group);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) add_row<BACC>(q[j], part);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t dead = k + j < group ? 0u : 0x80008000u;   // both halves -0.0
+        add_row<BACC>(G{q[j].x | dead, q[j].y | dead}, part);
+      }
     }
-    for (; k < group; ++k) add_row<BACC>(ld_tile<G, kGradNt>(g[base + k], at), part);
     if (base == 0) {
 #pragma unroll
       for (int e = 0; e < SV; ++e) acc[e] = part[e];
