@@ -332,32 +332,35 @@ __device__ __forceinline__ void add_row(u32x2 q, float (&x)[4]) {
   for (int e = 0; e < 4; ++e) x[e] = BACC ? round_bf16(x[e] + t[e]) : x[e] + t[e];
 }
 
+// x += row (add_row) for a row of the group; a row past it (it loaded nothing)
+// is skipped (live is uniform across the workgroup).
+template <bool BACC>
+__device__ __forceinline__ void add_chunk_row(u32x2 q, bool live, float (&x)[4]) {
+  if (live) add_row<BACC>(q, x);
+}
+
 // The general left fold, for hybrid sharding and for bf16 partial sums. Rows
 // [rho*group, (rho+1)*group) are one replica group: each group is folded on
 // its own (the reduce-scatter inside the group), then the group sums are
 // folded in group order (the all-reduce across groups), then scaled. With
 // BACC every addition is an fp32 add followed by rounding to bf16. A group's
-// first row starts its partial sum; the rest follow in chunks of 8, each
-// chunk's loads issued before its first add; in the last, partial chunk the
-// rows past the group load nothing and add -0.0, which changes no sum (the
-// partial is already a bf16 value when BACC, and -0.0 is the exact identity
-// of the add; a NaN partial is already quiet from the chunk's live rows).
+// rows are loaded in chunks of 8, each chunk's loads issued before its first
+// add; the group's first row starts its partial sum. In the last, partial
+// chunk the rows past the group load nothing and are not added.
 template <int SV, bool BACC>
 __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, int ng, int group,
                                                     float gs, At at, float (&acc)[SV]) {
   using G = u32x2;
   for (int base = 0; base < ng; base += group) {
     float part[SV];
-    unpack(ld_tile<G, kGradNt>(g[base], at), part);
-    for (int k = 1; k < group; k += 8) {   // g[base + k + 7]: inside the padded array
+    for (int k = 0; k < group; k += 8) {   // g[base + k + 7]: inside the padded array
       G q[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[j] = ld_tile<G, kGradNt>(g[base + k + j], at, k + j < group);
+      if (k == 0) unpack(q[0], part);
+      else add_chunk_row<BACC>(q[0], 0 < group - k, part);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t dead = k + j < group ? 0u : 0x80008000u;   // both halves -0.0
-        add_row<BACC>(G{q[j].x | dead, q[j].y | dead}, part);
-      }
+      for (int j = 1; j < 8; ++j) add_chunk_row<BACC>(q[j], j < group - k, part);
     }
     if (base == 0) {
 #pragma unroll
