@@ -144,3 +144,144 @@ def test_random_unit_every_element(i):
         gw = to_np(w)[:n]
         bad = np.flatnonzero(gw != np.asarray(want[3]))
         assert bad.size == 0, f"{what}: bf16 param: {bad.size} elements differ, first {bad[:5].tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# the copies: flatten/pad windows and unflatten, random units and placements
+# ---------------------------------------------------------------------------
+
+N_COPY_CASES = 64
+
+
+def draw_copy(i):
+    rng = np.random.default_rng(19000 + i)
+    shapes = []
+    for _ in range(int(rng.integers(1, 9))):
+        n = int(np.exp(rng.uniform(0, np.log(300_000))))
+        shapes.append((n,) if rng.random() < 0.6 or n < 4 else (int(rng.integers(1, 9)), n // 4 + 1))
+    F = int(rng.choice([1, 2, 3, 4, 7, 8, 13, 16]))
+    U = sum(int(np.prod(s)) for s in shapes)
+    S = -(-U // F)
+    begin = int(rng.integers(0, F * S))
+    length = int(rng.integers(0, F * S - begin + 1))
+    return dict(shapes=shapes, F=F, rank=int(rng.integers(0, F)), begin=begin, length=length,
+                dtype=str(rng.choice(["f32", "bf16"])), out=str(rng.choice(["f32", "bf16"])),
+                src_off=int(rng.integers(0, 8)), dst_off=int(rng.integers(0, 8)))
+
+
+def host_tensor_bits(rng_seed, shape, dtype):
+    rng = np.random.default_rng(rng_seed)
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        return rng.standard_normal(n).astype(np.float32).view(np.uint32)
+    return (rng.standard_normal(n).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def to_dev(bits, off):
+    """bits as a device tensor starting `off` elements into a larger buffer."""
+    tdtype = torch.int32 if bits.dtype == np.uint32 else torch.int16
+    fdtype = torch.float32 if bits.dtype == np.uint32 else torch.bfloat16
+    buf = torch.zeros(bits.size + 16, dtype=tdtype, device="cuda")
+    buf[off:off + bits.size] = torch.from_numpy(bits.view(np.int32 if bits.dtype == np.uint32
+                                                          else np.int16)).cuda()
+    return buf.view(fdtype)[off:off + bits.size]
+
+
+@pytest.mark.parametrize("i", range(N_COPY_CASES))
+def test_random_copies_every_element(i):
+    """flatten_pad of a random window of the padded flat buffer (tensors and the
+    destination at random element offsets), and unflatten of the F shards into
+    per-tensor outputs (fp32 or bf16 on each side), against the oracle, bit for bit,
+    with the bytes around each destination untouched."""
+    d = draw_copy(i)
+    u = fsdp.Unit(d["shapes"], d["F"], d["rank"])
+    L = O.unit_layout(d["shapes"], d["F"], d["rank"])
+    what = f"copy case {i}: {d}"
+    print(what, flush=True)
+    # flatten_pad: window [begin, begin + length) of the padded flat buffer
+    host = [host_tensor_bits(29000 + 31 * i + j, s, d["dtype"]) for j, s in enumerate(d["shapes"])]
+    dev = [to_dev(h, (d["src_off"] + j) % 8) for j, h in enumerate(host)]
+    want = O.flatten_pad(host, d["F"], d["begin"], d["length"])
+    sent = 0x7FC00001 if d["dtype"] == "f32" else 0x7FC1
+    dst_bits = np.full(d["length"] + 16, sent, dtype=np.uint32 if d["dtype"] == "f32" else np.uint16)
+    dst_buf = to_dev(dst_bits, 0)
+    dst = dst_buf[d["dst_off"]:d["dst_off"] + d["length"]]
+    fsdp.flatten_pad(u, dev, dst, begin=d["begin"], length=d["length"])
+    torch.cuda.synchronize()
+    got = to_np(dst_buf)
+    got = got.view(np.uint32) if got.dtype == np.float32 else got
+    o = d["dst_off"]
+    assert (got[:o] == sent).all() and (got[o + d["length"]:] == sent).all(), f"{what}: flatten guards"
+    bad = np.flatnonzero(got[o:o + d["length"]] != want)
+    assert bad.size == 0, f"{what}: flatten: {bad.size} differ, first {bad[:5].tolist()}"
+    # unflatten: the F shards of the whole padded buffer into per-tensor outputs
+    full = O.flatten_pad(host, d["F"])
+    S = L.S
+    shards = [to_dev(full[k * S:(k + 1) * S].copy(), (d["src_off"] + k) % 8) for k in range(d["F"])]
+    want_t = O.unflatten([full[k * S:(k + 1) * S].view(np.float32) if d["dtype"] == "f32"
+                          else full[k * S:(k + 1) * S] for k in range(d["F"])], L, d["shapes"],
+                         out=d["out"])
+    osent = 0x7FC00001 if d["out"] == "f32" else 0x7FC1
+    outs, bufs = [], []
+    for j, s in enumerate(d["shapes"]):
+        n = int(np.prod(s))
+        b = to_dev(np.full(n + 16, osent, dtype=np.uint32 if d["out"] == "f32" else np.uint16), 0)
+        oo = (d["dst_off"] + 3 * j) % 8
+        outs.append(b[oo:oo + n])
+        bufs.append((b, oo, n))
+    fsdp.unflatten(u, shards, outs)
+    torch.cuda.synchronize()
+    for j, ((b, oo, n), w_) in enumerate(zip(bufs, want_t)):
+        g = to_np(b)
+        g = g.view(np.uint32) if g.dtype == np.float32 else g
+        wb = np.asarray(w_).reshape(-1)
+        wb = wb.view(np.uint32) if wb.dtype == np.float32 else wb
+        assert (g[:oo] == osent).all() and (g[oo + n:] == osent).all(), f"{what}: tensor {j} guards"
+        bad = np.flatnonzero(g[oo:oo + n] != wb)
+        assert bad.size == 0, f"{what}: unflatten tensor {j}: {bad.size} differ, first {bad[:5].tolist()}"
+
+
+# ---------------------------------------------------------------------------
+# the batched many-unit step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_unit_lists_every_element(i):
+    """fsdp_reduce_adamw_units over a random list of units (small ones batched,
+    larger ones launched alone; rows and state at random placements), against the
+    oracle unit by unit, every element."""
+    rng = np.random.default_rng(39000 + i)
+    F = int(rng.choice([2, 4, 8]))
+    n_grads = int(rng.choice([F, max(1, F // 2), 8]))
+    steps, cases = [], []
+    for j in range(int(rng.integers(2, 12))):
+        big = rng.random() < 0.2
+        n = int(np.exp(rng.uniform(np.log(4_000_000) if big else 0,
+                                   np.log(9_000_000 if big else 300_000))))
+        shapes = [(n,)] if rng.random() < 0.5 else [(max(1, n // 3),), (max(1, n - n // 3),)]
+        case = Case(shapes, F, int(rng.integers(0, F)), n_grads=n_grads, config=700 + 16 * i + j)
+        u = fsdp.Unit(case.shapes, F, case.rank)
+        L = case.L
+        roff = int(rng.integers(0, 4))
+        rows = [torch.empty(L.U + 8, dtype=torch.bfloat16, device="cuda")[roff:roff + L.U]
+                for _ in range(n_grads)]
+        case.device_grads(1, out=rows)
+        flat = O.flatten_pad([t.view(np.uint32) for t in case.host_master_tensors()], F)
+        p = torch.from_numpy(flat.view(np.float32)[L.shard_begin:L.shard_begin + L.S].copy()).cuda()
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        w = torch.empty(L.S, dtype=torch.bfloat16, device="cuda") if rng.random() < 0.7 else None
+        steps.append((u, rows, p, m, v, w))
+        cases.append(case)
+    fsdp.reduce_adamw_units(steps, fsdp.AdamWHparams(**HP.__dict__), 1)
+    torch.cuda.synchronize()
+    for j, (case, (u, rows, p, m, v, w)) in enumerate(zip(cases, steps)):
+        n = case.L.shard_valid
+        if n == 0:
+            continue
+        want = case.oracle_full(1, emit=w is not None)[-1]
+        for got, exp, name in zip((p, m, v), want[:3], ("master", "exp_avg", "exp_avg_sq")):
+            bad = np.flatnonzero(to_np(got)[:n].view(np.uint32) != np.asarray(exp).view(np.uint32))
+            assert bad.size == 0, f"list {i} unit {j} (U={case.L.U}): {name}: {bad.size} differ"
+        if w is not None:
+            bad = np.flatnonzero(to_np(w)[:n] != np.asarray(want[3]))
+            assert bad.size == 0, f"list {i} unit {j}: bf16 param: {bad.size} differ"
