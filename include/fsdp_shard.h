@@ -18,9 +18,16 @@
  *   real (non-pad) elements in rank r's window = clamp(U - r*S, 0, S).
  * - bf16 buffers are passed as raw 16-bit patterns; fp32 as IEEE binary32.
  * - Device pointers are plain device addresses (e.g. torch data_ptr()). Any
- *   element-aligned address is accepted; 16-byte aligned buffers take the
- *   128-bit vector path. Arrays of pointers (grads, shards, tensors) are HOST
- *   arrays of device pointers, copied into kernel arguments by the call.
+ *   element-aligned address is accepted. The step calls take their vector
+ *   path when the fp32 buffers are 16-byte aligned (8-byte for a bf16 output)
+ *   and every gradient row's rank window starts on an 8-byte boundary; rows
+ *   that are only 2-byte aligned take a shifted-row path (flat folds) or the
+ *   scalar path (grouped folds), and state off 16-byte alignment takes the
+ *   scalar path. Windows that start off a 128-byte line are read and written
+ *   with their tiles in runs per XCD, which keeps the cost of the lines they
+ *   share with neighbouring tiles near 3% of the row bytes. Arrays of pointers
+ *   (grads, shards, tensors) are HOST arrays of device pointers, copied into
+ *   kernel arguments by the call.
  * - Ownership: the caller owns every device buffer. The library owns only the
  *   opaque fsdp_unit (host memory) and allocates no device memory.
  * - Execution: every device entry point only enqueues work on `stream`
