@@ -78,14 +78,6 @@
 #ifndef FSDP_COPY_STORE_CPOL
 #define FSDP_COPY_STORE_CPOL 18
 #endif
-// The step kernels' bf16 parameter output (the emission): a device-scope store
-// without the streaming hint (sc1), so its lines may stay in the memory-side
-// cache for the gather that reads them next. With the streaming hint the
-// output's 2 bytes per element cost the fused step about 4 us more on the 7B
-// block (25M elements), and the whole step (fused + gather) 3-4 us more.
-#ifndef FSDP_EMIT_STORE_CPOL
-#define FSDP_EMIT_STORE_CPOL 16
-#endif
 
 // Resident 256-thread workgroups per CU of the batched many-unit fused kernel
 // (0: no cap), imposed with unused dynamic LDS on batches of at least
@@ -176,7 +168,6 @@ __device__ __forceinline__ void st(void* p, V x) {
   else *reinterpret_cast<V*>(p) = x;
 }
 constexpr int kStepCpol = FSDP_STEP_STORE_CPOL;
-constexpr int kEmitCpol = FSDP_EMIT_STORE_CPOL;
 constexpr int kCopyCpol = FSDP_COPY_STORE_CPOL;
 constexpr bool kGradNt = FSDP_GRAD_NT_LOAD != 0;
 constexpr bool kCopyNtLoad = FSDP_COPY_NT_LOAD != 0;
@@ -251,7 +242,7 @@ __device__ __forceinline__ void out_f32(float* base, int64_t t0, int64_t len, in
 __device__ __forceinline__ void out_bf16(uint16_t* base, int64_t t0, int64_t len, int64_t i,
                                          const float (&x)[4]) {
   const u32x2 b = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-  if constexpr (kEmitCpol >= 0) bst<kEmitCpol>(rsrc(base + t0, 2 * len), int(2 * (i - t0)), b);
+  if constexpr (kStepCpol >= 0) bst<kStepCpol>(rsrc(base + t0, 2 * len), int(2 * (i - t0)), b);
   else st<u32x2, true>(base + i, b);
 }
 

@@ -5,9 +5,8 @@
 // the fused kernel's lane layout (4 consecutive elements per lane: one 8-byte
 // load per row, one 16-byte load or store per fp32 array, one 8-byte bf16
 // store), its load hints (streaming on the rows, ordinary on the fp32 arrays),
-// its stores (device-scope buffer stores bounded to the workgroup's tile:
-// streaming for the fp32 arrays, without the streaming hint for the bf16
-// output) and a caller-chosen workgroup size and per-CU cap. What it
+// its stores (device-scope streaming buffer stores bounded to the
+// workgroup's tile) and a caller-chosen workgroup size and per-CU cap. What it
 // computes is only a pass-through that keeps every load live: p + (sum of the
 // rows), m and v unchanged, and the high half of the new p as the bf16 value.
 // Its time is the stream-mix ceiling the fused kernel is compared with.
@@ -23,8 +22,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 8;
-constexpr int kCpol = 18;       // sc1 nt: device-scope streaming store (the fp32 arrays)
-constexpr int kEmitCpol = 16;   // sc1: device-scope store (the bf16 output)
+constexpr int kCpol = 18;   // sc1 nt: device-scope streaming store
 
 struct Args {
   const uint16_t* g[kRows];
@@ -71,7 +69,7 @@ __global__ __launch_bounds__(256) void k_stream_mix(Args a) {
   __builtin_amdgcn_raw_buffer_store_b128(po, rsrc(a.p + t0, 4 * tl), off, 0, kCpol);
   __builtin_amdgcn_raw_buffer_store_b128(mo, rsrc(a.m + t0, 4 * tl), off, 0, kCpol);
   __builtin_amdgcn_raw_buffer_store_b128(vo, rsrc(a.v + t0, 4 * tl), off, 0, kCpol);
-  __builtin_amdgcn_raw_buffer_store_b64(wo, rsrc(a.w + t0, 2 * tl), off / 2, 0, kEmitCpol);
+  __builtin_amdgcn_raw_buffer_store_b64(wo, rsrc(a.w + t0, 2 * tl), off / 2, 0, kCpol);
 }
 
 }  // namespace
