@@ -1,10 +1,13 @@
 """Test cases for the GPU parity tests: device inputs and oracle expectations.
 
 Inputs come from ``datagen`` (the host generator for the oracle, its device
-twin to fill HBM). Expected values come only from ``oracle`` evaluated on
+twin to fill HBM). Expected values come only from ``oracle``, evaluated on
 host-generated inputs, either on whole (small) units or on sampled indices of
 full-size units: every step of the path is elementwise in the shard index, so
 a sampled index's whole multi-step trajectory can be recomputed on its own.
+The every-element checks of full-size units feed the oracle host copies of the
+device twin's fills instead (regenerating billions of values on the host takes
+minutes), after spot-checking those fills against the host generator.
 """
 
 from __future__ import annotations
@@ -270,8 +273,9 @@ class ModelShard:
         return sum(t.numel() * t.element_size() for t in (self.p, self.m, self.v, self.w,
                                                           self.gslot))
 
-    def oracle_sampled(self, u, loc):
-        """Oracle's first step of unit u at local shard indices loc."""
+    def inputs_at(self, u, loc):
+        """Unit u's master and gradient-row values at local shard indices loc,
+        regenerated on the host: (master fp32, [bf16 bits of row k])."""
         L = self.L[u]
         g = L.shard_begin + np.asarray(loc, dtype=np.int64)
         offs = np.asarray(L.offsets, dtype=np.int64)
@@ -284,6 +288,12 @@ class ModelShard:
         base = 100 if u == len(self.L) - 1 else 0
         rows = [datagen.bf16_bits_host(self.grad_seed, base + k, g, W.GRAD_SIGMA)
                 for k in range(self.F)]
+        return p, rows
+
+    def oracle_sampled(self, u, loc):
+        """Oracle's first step of unit u at local shard indices loc."""
+        p, rows = self.inputs_at(u, loc)
+        g = np.asarray(loc, dtype=np.int64)
         z = np.zeros_like(p)
         one = O.unit_layout([(g.size,)], 1, 0)
         return O.reduce_adamw_shard(rows, one, p, z, z, HP, 1, grad_scale=1.0 / self.F,

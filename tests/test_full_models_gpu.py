@@ -4,9 +4,12 @@
   embedding, final norm, lm_head), F=8, rank 0, ~842M params;
 * Llama-70B-shaped rank shard: 80 GQA block units + root, F=8, rank 0,
   ~8.62B params (~138 GB of persistent state resident in HBM).
-One fused reduce + AdamW + bf16 step per unit on one stream; sampled indices
-of every unit (all of them in the named units) are checked against the
-oracle. Persistent bytes allocated equal 16 * sum(S) per the pages' budget.
+One fused reduce + AdamW + bf16 step per unit on one stream. Every element of
+the named units and of the root unit is checked against the oracle (run on
+host copies of the generator's device fills, which are spot-checked against
+its host form first), and sampled indices of every other unit (with the
+oracle's inputs regenerated on the host). Persistent bytes allocated equal
+16 * sum(S) per the pages' budget.
 """
 
 import gc
@@ -17,7 +20,8 @@ import torch
 
 import datagen
 from datagen import workloads as W
-from shard_cases import ModelShard, assert_bf16_ulp, assert_rel, gather
+from oracle import fsdp_oracle as O
+from shard_cases import HP, ModelShard, assert_bf16_ulp, assert_bits, assert_rel, gather, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +33,37 @@ import sharded_flatparameter_flatten_amd as fsdp  # noqa: E402
 HPD = fsdp.AdamWHparams(**W.ADAMW)
 
 
+def check_every_element(ms, i, p_before, what):
+    """Unit i's window after the step against the oracle on every element. The
+    oracle's inputs are host copies of the device fills (the rank window of
+    each gradient row and the master before the step), each spot-checked
+    against the host generator."""
+    L = ms.L[i]
+    lo, n = L.shard_begin, L.shard_valid
+    rows = [to_np(g[lo:lo + n]) for g in ms.grads(i)]
+    loc = ms.sample(i, 4096, seed=1000 + i)
+    want_in = ms.inputs_at(i, loc)
+    for k in (0, ms.F - 1):
+        assert_bits(rows[k][loc], want_in[1][k], f"{what} row {k} fill")
+    assert_bits(p_before[loc].view(np.uint32), want_in[0].view(np.uint32), f"{what} master fill")
+    z = np.zeros(n, np.float32)
+    want = O.reduce_adamw_shard(rows, O.unit_layout([(n,)], 1, 0), p_before, z, z.copy(), HP,
+                                1, grad_scale=1.0 / ms.F, emit_bf16=True)
+    assert_rel(to_np(ms.window(ms.p, i))[:n], want[0], what=what + " master (every element)")
+    assert_rel(to_np(ms.window(ms.m, i))[:n], want[1], what=what + " exp_avg (every element)")
+    assert_rel(to_np(ms.window(ms.v, i))[:n], want[2], what=what + " exp_avg_sq (every element)")
+    assert_bf16_ulp(to_np(ms.window(ms.w, i))[:n], want[3], what=what + " bf16 (every element)")
+
+
 def run_model(name, full_units, sparse_n, multi=False):
     wl = W.WORKLOADS[name]
     ms = ModelShard(wl["units"], wl["F"], wl["rank"], wl["config"])
     units = [fsdp.Unit(W.shapes(u), wl["F"], wl["rank"]) for u in wl["units"]]
     assert [u.S for u in units] == [L.S for L in ms.L]
+    n_units = len(units)
+    full_units = set(full_units) | {n_units - 1}
+    torch.cuda.synchronize()
+    p_before = {i: to_np(ms.window(ms.p, i))[:units[i].shard_valid] for i in sorted(full_units)}
     if multi:
         fsdp.reduce_adamw_units([(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
                                   ms.window(ms.v, i), ms.window(ms.w, i))
@@ -43,12 +73,13 @@ def run_model(name, full_units, sparse_n, multi=False):
             fsdp.reduce_adamw_shard(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
                                     ms.window(ms.v, i), ms.window(ms.w, i), HPD, 1)
     torch.cuda.synchronize()
-    n_units = len(units)
     for i in range(n_units):
-        full = i in full_units or i == n_units - 1
-        loc = ms.sample(i, 1 << 15 if full else sparse_n, seed=i)
-        want = ms.oracle_sampled(i, loc)
         what = f"{name} unit {i}"
+        if i in full_units:
+            check_every_element(ms, i, p_before.pop(i), what)
+            print(f"{what}: every element of {units[i].shard_valid:,} checked", flush=True)
+        loc = ms.sample(i, sparse_n, seed=i)
+        want = ms.oracle_sampled(i, loc)
         assert_rel(gather(ms.window(ms.p, i), loc), want[0], what=what + " master")
         assert_rel(gather(ms.window(ms.m, i), loc), want[1], what=what + " exp_avg")
         assert_rel(gather(ms.window(ms.v, i), loc), want[2], what=what + " exp_avg_sq")
