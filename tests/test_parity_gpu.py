@@ -8,8 +8,9 @@ Bars (the stated tolerances for this path's numerics):
 * emitted bf16 parameters: <= 1 bf16 ulp.
 Small units are compared on every element. The 7B block at F=8 is compared on
 every element of every rank for one step, and on sampled indices over two
-steps; the F sweep on sampled indices of every rank; all in the launch
-configuration the bench uses. Also here: the tensor-count limit, other
+steps; the F sweep on every element of every rank (and on sampled indices
+against host-regenerated inputs); all in the launch configuration the bench
+uses. Also here: the tensor-count limit, other
 hyper-parameters and step numbers, and the fp32 -> bf16 rounding over all 2^32
 fp32 patterns.
 """
@@ -456,6 +457,49 @@ def test_blk7_f8_every_rank_every_element(blk7_grads):
     want = O.unflatten([to_np(w) for w in emitted], O.unit_layout(shapes, F, 0), shapes)
     for i, (o, e) in enumerate(zip(outs, want)):
         assert_bits(to_np(o).reshape(-1), np.asarray(e).reshape(-1), f"gathered tensor {i}")
+
+
+@pytest.fixture(scope="module")
+def sweep_master_host():
+    """Host copy of the sweep's master tensors as the device twin fills them
+    (the same for every F), spot-checked against the host generator."""
+    case = Case(W.shapes(W.BLK7), 1, 0, config=3, outliers=True)
+    masters = case.device_master_tensors()
+    host = [to_np(t) for t in masters]
+    del masters
+    idx = np.unique(np.concatenate([np.random.default_rng(11).integers(0, case.L.U, 8192),
+                                    np.arange(8), case.L.U - 1 - np.arange(8)]))
+    flat = np.concatenate(host)
+    assert_bits(flat[idx].view(np.uint32), case.host_master_at(idx).view(np.uint32),
+                "sweep master fill")
+    yield host
+    del host, flat
+
+
+@pytest.mark.parametrize("F", [1, 2, 4, 8, 16, 64, 7, 11, 13])
+def test_blk7_sharding_factor_sweep_every_element(F, sweep_grads, sweep_master_host):
+    """Every element of every rank of every sharding factor, one fused step with
+    emission. The oracle runs on host copies of the device fills (rows
+    spot-checked here, masters in the fixture)."""
+    shapes = W.shapes(W.BLK7)
+    flat = O.flatten_pad([t.view(np.uint32) for t in sweep_master_host], F).view(np.float32)
+    for rank in range(F):
+        case = Case(shapes, F, rank, config=3, outliers=True)
+        L = case.L
+        lo, n = L.shard_begin, L.shard_valid
+        u, p, m, v, w = run_rank(case, 1, grads_buf=sweep_grads[:F], grads_ready=True)
+        rows = [to_np(g[lo:lo + n]) for g in sweep_grads[:F]]
+        loc = case.sample_indices(2048, seed=F * 64 + rank + 1)
+        want_rows = case.host_grads_at(1, lo + loc)
+        for k in {0, F - 1}:
+            assert_bits(rows[k][loc], want_rows[k], f"F={F} rank={rank} row {k} fill")
+        z = np.zeros(n, np.float32)
+        want = O.reduce_adamw_shard(rows, O.unit_layout([(n,)], 1, 0), flat[lo:lo + n].copy(),
+                                    z, z.copy(), HP, 1, grad_scale=1.0 / F, emit_bf16=True)
+        fr = compare_full(case, (u, p, m, v, w), want)
+        if rank in (0, F - 1):
+            log(f"sweep F={F} rank={rank}: every element of {n:,}, bit-equal fractions {fr}")
+        del p, m, v, w, rows, want
 
 
 @pytest.mark.parametrize("F", [1, 2, 4, 8, 16, 64, 7, 11, 13])
