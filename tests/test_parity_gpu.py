@@ -721,20 +721,50 @@ def test_hybrid_reduce_shard_every_element(R, F, rank):
     assert_bits(to_np(out)[:u.shard_valid].view(np.uint32), want.view(np.uint32), "hybrid reduce")
 
 
-def test_hybrid_blk7_two_groups_of_8_sampled():
-    case = Case(W.shapes(W.BLK7), 8, 5, config=32, replicas=2)
-    u = fsdp.Unit(case.shapes, 8, 5)
-    grads = case.device_grads(1)
-    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
-    fsdp.flatten_pad(u, case.device_master_tensors(), p)
-    m, v = torch.zeros_like(p), torch.zeros_like(p)
-    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
-    fsdp.reduce_adamw_shard_hybrid(u, 2, grads, p, m, v, w, HPD, 1)
+def blk7_every_rank_every_element(config, step_fn, **case_kw):
+    """One fused step of the 7B block at F=8 on every rank, compared with the
+    oracle on every element. The oracle runs on host copies of the device
+    fills (gradient rows and master tensors), spot-checked against the host
+    generator first; step_fn(u, grads, p, m, v, w) calls the library."""
+    shapes, F = W.shapes(W.BLK7), 8
+    case0 = Case(shapes, F, 0, config=config, **case_kw)
+    grads = case0.device_grads(1)
+    masters = case0.device_master_tensors()
     torch.cuda.synchronize()
-    loc = case.sample_indices()
-    want = case.oracle_sampled(loc, 1)[-1]
-    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
-        assert_bits(_bits(gather(got, loc)), _bits(exp), f"hybrid blk7 {name}")
+    U = case0.L.U
+    idx = np.unique(np.concatenate([np.random.default_rng(config).integers(0, U, 4096),
+                                    np.arange(8), U - 1 - np.arange(8)]))
+    want_rows = case0.host_grads_at(1, idx)
+    for k in (0, len(grads) - 1):
+        assert_bits(gather(grads[k], idx), want_rows[k], f"row {k} fill")
+    host_m = [to_np(t) for t in masters]
+    assert_bits(np.concatenate(host_m)[idx].view(np.uint32),
+                case0.host_master_at(idx).view(np.uint32), "master fill")
+    rows = [to_np(g) for g in grads]
+    flat = O.flatten_pad([t.view(np.uint32) for t in host_m], F).view(np.float32)
+    del host_m
+    for rank in range(F):
+        case = Case(shapes, F, rank, config=config, **case_kw)
+        u = fsdp.Unit(shapes, F, rank)
+        p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+        fsdp.flatten_pad(u, masters, p)
+        m, v = torch.zeros_like(p), torch.zeros_like(p)
+        w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+        step_fn(u, grads, p, m, v, w)
+        torch.cuda.synchronize()
+        lo, n = u.shard_begin, u.shard_valid
+        z = np.zeros(n, np.float32)
+        want = case._step(rows, case.L, flat[lo:lo + n].copy(), z, z.copy(), 1, True)
+        for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+            assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"blk7 rank {rank} {name}")
+        log(f"blk7 F=8 rank {rank}: every element of {n:,} bit-equal")
+        del p, m, v, w, want
+
+
+def test_hybrid_blk7_two_groups_of_8_every_rank_every_element():
+    blk7_every_rank_every_element(
+        32, lambda u, g, p, m, v, w: fsdp.reduce_adamw_shard_hybrid(u, 2, g, p, m, v, w, HPD, 1),
+        replicas=2)
 
 
 # ---------------------------------------------------------------------------
@@ -776,20 +806,10 @@ def test_bf16acc_reduce_shard_every_element_and_coarser_than_fp32(ng):
     assert not np.array_equal(want, O.reduce_shard(host, case.L))
 
 
-def test_bf16acc_blk7_sampled():
-    case = Case(W.shapes(W.BLK7), 8, 3, config=42, outliers=True, bf16acc=True)
-    u = fsdp.Unit(case.shapes, 8, 3)
-    grads = case.device_grads(1)
-    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
-    fsdp.flatten_pad(u, case.device_master_tensors(), p)
-    m, v = torch.zeros_like(p), torch.zeros_like(p)
-    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
-    fsdp.reduce_adamw_shard_bf16acc(u, grads, p, m, v, w, HPD, 1)
-    torch.cuda.synchronize()
-    loc = case.sample_indices()
-    want = case.oracle_sampled(loc, 1)[-1]
-    for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
-        assert_bits(_bits(gather(got, loc)), _bits(exp), f"bf16acc blk7 {name}")
+def test_bf16acc_blk7_every_rank_every_element():
+    blk7_every_rank_every_element(
+        42, lambda u, g, p, m, v, w: fsdp.reduce_adamw_shard_bf16acc(u, g, p, m, v, w, HPD, 1),
+        outliers=True, bf16acc=True)
 
 
 @pytest.mark.parametrize("n_grads", [8, 11, 24])
