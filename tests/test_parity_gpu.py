@@ -7,9 +7,10 @@ Bars (the stated tolerances for this path's numerics):
   report the bit-equal fraction);
 * emitted bf16 parameters: <= 1 bf16 ulp.
 Small units are compared on every element. The 7B block at F=8 is compared on
-every element of every rank for one step, and on sampled indices over two
-steps; the F sweep on every element of every rank (and on sampled indices
-against host-regenerated inputs); all in the launch configuration the bench
+every element of every rank for one step (also with hybrid 2 x 8 rows and with
+bf16 partial sums), and on every element of three ranks over two steps; the F
+sweep on every element of every rank; full-size inputs also on sampled indices
+against host-regenerated inputs; all in the launch configuration the bench
 uses. Also here: the tensor-count limit, other
 hyper-parameters and step numbers, and the fp32 -> bf16 rounding over all 2^32
 fp32 patterns.
@@ -359,17 +360,51 @@ def sweep_grads():
 
 
 @pytest.mark.parametrize("rank", [0, 3, 7])
-def test_blk7_f8_two_steps_sampled(rank, blk7_grads):
+def test_blk7_f8_two_steps(rank, blk7_grads):
+    """Two fused steps (fresh gradients each step, so step 2 starts from non-zero
+    m and v): every element after each step against the oracle on host copies
+    of the device fills (spot-checked against the host generator), and sampled
+    indices after step 2 against the oracle on host-regenerated inputs."""
     case = Case(W.shapes(W.BLK7), 8, rank, config=1)
+    L = case.L
+    lo, n = L.shard_begin, L.shard_valid
     log(f"blk7 F=8 rank={rank}")
-    u, p, m, v, w = run_rank(case, 2, grads_buf=blk7_grads[:8])
+    u = fsdp.Unit(case.shapes, 8, rank)
+    masters = case.device_master_tensors()
+    torch.cuda.synchronize()
+    host_m = [to_np(t) for t in masters]
+    spot = case.sample_indices(2048, seed=rank + 100)
+    hp_ = np.concatenate(host_m)[lo + spot]
+    assert_bits(hp_.view(np.uint32), case.host_master_at(lo + spot).view(np.uint32), "master fill")
+    hp = O.flatten_pad([t.view(np.uint32) for t in host_m], 8).view(np.float32)[lo:lo + n].copy()
+    del host_m
+    p = torch.empty(u.S, dtype=torch.float32, device=DEV)
+    fsdp.flatten_pad(u, masters, p)
+    del masters
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
+    hm, hv = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    one = O.unit_layout([(n,)], 1, 0)
+    for t in (1, 2):
+        grads = case.device_grads(t, out=blk7_grads[:8])
+        fsdp.reduce_adamw_shard(u, grads, p, m, v, w, HPD, t)
+        torch.cuda.synchronize()
+        rows = [to_np(g[lo:lo + n]) for g in grads]
+        want_rows = case.host_grads_at(t, lo + spot)
+        for k in (0, 7):
+            assert_bits(rows[k][spot], want_rows[k], f"step {t} row {k} fill")
+        want = O.reduce_adamw_shard(rows, one, hp, hm, hv, HP, t, grad_scale=1.0 / 8,
+                                    emit_bf16=True)
+        hp, hm, hv = want[:3]
+        fr = compare_full(case, (u, p, m, v, w), want)
+        log(f"step {t}: every element of {n:,}, bit-equal fractions {fr}")
+        del rows
     loc = case.sample_indices()
     want = case.oracle_sampled(loc, 2)[-1]
-    fr = [assert_rel(gather(p, loc), want[0], what="master"),
-          assert_rel(gather(m, loc), want[1], what="exp_avg"),
-          assert_rel(gather(v, loc), want[2], what="exp_avg_sq"),
-          assert_bf16_ulp(gather(w, loc), want[3], what="bf16 param")]
-    log("bit-equal fractions", fr, "samples", loc.size)
+    assert_rel(gather(p, loc), want[0], what="master")
+    assert_rel(gather(m, loc), want[1], what="exp_avg")
+    assert_rel(gather(v, loc), want[2], what="exp_avg_sq")
+    assert_bf16_ulp(gather(w, loc), want[3], what="bf16 param")
 
 
 def test_blk7_f8_fused_equals_unfused_full_shard(blk7_grads):
@@ -381,7 +416,11 @@ def test_blk7_f8_fused_equals_unfused_full_shard(blk7_grads):
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), name
 
 
-def test_blk7_cast_unflatten_full_size_sampled():
+def test_blk7_cast_unflatten_full_size():
+    """The gather of 8 fp32 shards of the 7B block into its 9 bf16 tensors:
+    sampled indices against the oracle's rounding of host-regenerated values,
+    and every element against the oracle's unflatten of host copies of the
+    shards."""
     shapes = W.shapes(W.BLK7)
     F = 8
     u = fsdp.Unit(shapes, F, 0)
@@ -407,6 +446,10 @@ def test_blk7_cast_unflatten_full_size_sampled():
             src[sel] = datagen.normal_f32_host(seed, int(kk), g[sel] - kk * u.S, 0.02)
         want = O.bf16_round_nearest_even(src)
         assert_bits(gather(o.reshape(-1), j), want, f"tensor {i}")
+    want = O.unflatten([to_np(s_) for s_ in shards], O.unit_layout(shapes, F, 0), shapes,
+                       out="bf16")
+    for i, (o, e) in enumerate(zip(outs, want)):
+        assert_bits(to_np(o).reshape(-1), np.asarray(e).reshape(-1), f"tensor {i} every element")
 
 
 def test_blk7_f8_every_rank_every_element(blk7_grads):
