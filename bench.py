@@ -385,9 +385,9 @@ def stream_mix_leg(torch, stream, sets, u, rank, F, gather, first, L):
     lib.probe_stream_mix.restype = ctypes.c_int
     lib.probe_stream_mix.argtypes = [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_void_p] * 4 + \
         [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    # the library's shape for this launch: one-wave workgroups, as many per CU as
-    # 1280 bytes over the 168 bytes a lane moves per tile (8 rows + state + bf16)
-    threads, wg_per_cu = 64, 8
+    # the library's shape for this launch: one-wave workgroups, 10 per CU (the
+    # staged fused step's count)
+    threads, wg_per_cu = 64, 10
     R = len(sets)
     rows = []
     for grads, p, m, v, shards, outs in sets:
@@ -757,6 +757,14 @@ def _request_bytes(rd, wr):
     return read, write
 
 
+def fused_kernel_re(F: int):
+    """The fused reduce+AdamW+bf16 emit kernel of an F-row flat fold, by its
+    demangled name in rocprofv3 output: the one-tile kernel of the staged fused
+    step (8 or 16 rows), or the general vector kernel (other counts)."""
+    return re.compile(r"k_step_one<%d, true(, 0, false)?>|"
+                      r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % (F, F))
+
+
 def pmc_summary(read_dir: str, write_dir: str, F: int = 8):
     """Prints the traffic summary (markdown + JSON block) from two rocprofv3
     --pmc runs of `bench.py --quick`: one with READ_COUNTERS, one with
@@ -770,7 +778,7 @@ def pmc_summary(read_dir: str, write_dir: str, F: int = 8):
     both must come out within 0.1% of 2^30 bytes read and written."""
     import datagen.workloads as W
 
-    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % F)
+    fused = fused_kernel_re(F)
     rr, wr = _counter_rows(read_dir), _counter_rows(write_dir)
     kinds = {
         "fused": lambda n: bool(fused.search(n)),
@@ -810,7 +818,7 @@ def pmc_summary(read_dir: str, write_dir: str, F: int = 8):
     alg_r, alg_w = (2 * F + 12) * valid, 14 * valid
     f, g = per["fused"], per["gather"]
     rec = {
-        "kernel": "k_step_vec<Fused, %d, emit> (fused reduce+AdamW+bf16 emit)" % F,
+        "kernel": "k_step_one<%d, emit> (fused reduce+AdamW+bf16 emit)" % F,
         "workload": "7B block unit, F=%d, rank 0, shard %d" % (F, valid),
         "kernels_hip_sha256_16": kernel_source_hash(),
         "read_request_bytes": READ_REQUEST_BYTES,
@@ -865,7 +873,7 @@ def trace_steps(trace_csv: str, warmup: int, steps: int, F: int = 8):
     Prints one JSON line with avg/median/p10/p90/min in us per kernel."""
     import csv
 
-    fused = re.compile(r"k_step_vec<\(\(anonymous namespace\)::Op\)2, %d, true(, 0, false)?>" % F)
+    fused = fused_kernel_re(F)
     rows = list(csv.DictReader(open(trace_csv)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     lib = [r for r in rows if "k_step" in r["Kernel_Name"] or "k_segcopy" in r["Kernel_Name"]]
@@ -1155,7 +1163,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "fused reduce+AdamW+bf16 emit (k_step_vec<Fused, 8, emit>)",
+            "kernel": "fused reduce+AdamW+bf16 emit (k_step_one<8, emit>)",
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

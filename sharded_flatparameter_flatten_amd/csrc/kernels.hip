@@ -24,9 +24,10 @@
 //  * occupancy, also chosen by measurement (step_shape below): long launches
 //    of the reduce, AdamW and fused kernels run one-wave workgroups
 //    (256-element tiles), as many per CU as keep about 80 KiB of loads and
-//    stores in flight per CU (8 for the fused step with 8 rows); the per-CU
-//    counts are held down by unused dynamic LDS sized from the device's LDS
-//    per CU;
+//    stores in flight per CU, except the fused step with 8 or more rows,
+//    which stages its tile loads (8 rows at a time, then the fp32 state) and
+//    runs 10 per CU in a one-tile kernel; the per-CU counts are held down by
+//    unused dynamic LDS sized from the device's LDS per CU;
 //  * buffers that are not aligned (e.g. a rank window r*S with S odd) take a
 //    lane-strided scalar path, still coalesced per instruction;
 //  * the gather/unflatten and flatten/pad copies are planned on the host as
@@ -98,6 +99,12 @@
 // (folded flat in chunks of 8 rows) on 2^FSDP_CAP_MIN_LOG2+ elements.
 #ifndef FSDP_CHUNKED_WG_PER_CU
 #define FSDP_CHUNKED_WG_PER_CU 12
+#endif
+
+// One-wave workgroups per CU for the fused step with a compile-time fold of 8
+// or more rows (its tile loads staged: see step_tile).
+#ifndef FSDP_STAGED_WG_PER_CU
+#define FSDP_STAGED_WG_PER_CU 10
 #endif
 
 using fsdp::fail;
@@ -272,7 +279,9 @@ enum class Op { Reduce, AdamW, Fused };
 
 // Left fold of the gradient rows for SV consecutive elements of a tile,
 // times gs. NG > 0 is the compile-time count: every row load is issued (and
-// held issued by a scheduling barrier) before the first add. NG == 0 reads the
+// held issued by a scheduling barrier) before the first add; with STAGE the
+// rows go in stages of up to 8 instead, each stage's loads issued together and
+// added before the next stage is issued (same adds, same order). NG == 0 reads the
 // count at run time and folds chunks of 8 rows, each chunk's loads issued
 // before its first add. That fold starts from -0.0, the exact identity of IEEE
 // addition (-0 + x is x for every x, -0, infinities and NaN included), so its
@@ -281,11 +290,26 @@ enum class Op { Reduce, AdamW, Fused };
 // descriptor) and add -0.0. Reading g[k + j] there stays inside the array: the
 // chunk starts at a multiple of 8 below n_grads <= FSDP_MAX_RANKS, so its last
 // pointer is below FSDP_MAX_RANKS.
-template <int NG, int SV>
+template <int NG, int SV, bool STAGE = false>
 __device__ __forceinline__ void reduce_rows(const uint16_t* const* g, int ng, float gs,
                                             At at, float (&acc)[SV]) {
   using G = u32x2;
-  if constexpr (NG > 0) {
+  if constexpr (NG > 0 && STAGE) {
+    constexpr int C = NG < 8 ? NG : 8;
+    static_assert(NG % C == 0, "whole stages");
+#pragma unroll
+    for (int c = 0; c < NG; c += C) {
+      G q[C];
+#pragma unroll
+      for (int k = 0; k < C; ++k) q[k] = ld_tile<G, kGradNt>(g[c + k], at);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c == 0) unpack(q[0], acc);
+      else accumulate(q[0], acc);
+#pragma unroll
+      for (int k = 1; k < C; ++k) accumulate(q[k], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (NG > 0) {
     G q[NG];
 #pragma unroll
     for (int k = 0; k < NG; ++k) q[k] = ld_tile<G, kGradNt>(g[k], at);
@@ -376,12 +400,40 @@ __device__ __forceinline__ void reduce_rows_general(const uint16_t* const* g, in
 
 // The grouped fold of reduce_rows_general with compile-time counts: NG rows in
 // groups of GRP (GRP == NG: one group, i.e. the flat fold with bf16 partials),
-// all NG row loads issued before the first add. Same operations in the same
-// order as reduce_rows_general.
-template <int NG, int GRP, bool BACC>
+// all NG row loads issued before the first add, or with STAGE in stages of 8
+// rows as in reduce_rows. Same operations in the same order as
+// reduce_rows_general.
+template <int NG, int GRP, bool BACC, bool STAGE = false>
 __device__ __forceinline__ void reduce_rows_grouped(const uint16_t* const* g, float gs, At at,
                                                     float (&acc)[4]) {
   static_assert(NG % GRP == 0, "whole groups");
+  if constexpr (STAGE) {
+    constexpr int C = NG < 8 ? NG : 8;
+    static_assert(NG % C == 0, "whole stages");
+    float part[4];
+#pragma unroll
+    for (int c = 0; c < NG; c += C) {
+      u32x2 q[C];
+#pragma unroll
+      for (int k = 0; k < C; ++k) q[k] = ld_tile<u32x2, kGradNt>(g[c + k], at);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < C; ++k) {
+        const int r = c + k;                     // row index, a compile-time constant
+        if (r % GRP == 0) unpack(q[k], part);
+        else add_row<BACC>(q[k], part);
+        if (r % GRP == GRP - 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e] = r < GRP ? part[e] : (BACC ? round_bf16(acc[e] + part[e]) : acc[e] + part[e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * gs;
+    return;
+  }
   u32x2 q[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) q[k] = ld_tile<u32x2, kGradNt>(g[k], at);
@@ -519,6 +571,63 @@ __device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
   return int64_t(j / kShiftRun) * (8 * kShiftRun) + (b % 8) * kShiftRun + j % kShiftRun;
 }
 
+// Whether the fused step stages its tile loads: the gradient rows in stages of
+// 8 (each added before the next is issued), then the fp32 state. Measured on
+// MI355X with rotating buffer sets, a wave that issues its 8 or 16 rows and
+// its state at once (64-80% of a tile's loads in one burst) kept the stream
+// mix 1-2% below a wave that keeps at most 8 rows' or the state's loads in
+// flight, with 10 rather than 8 one-wave workgroups per CU.
+template <Op OP, int NG>
+constexpr bool staged_tile() { return OP == Op::Fused && NG >= 8; }
+
+// One workgroup tile of the vector path: elements [t0, t0 + tl), lane element i.
+template <Op OP, int NG, bool EMIT, int GRP, bool BACC>
+__device__ __forceinline__ void step_tile(const StepArgs& a, int64_t t0, int64_t tl, int64_t i) {
+  const At at{t0, tl, uint32_t(threadIdx.x) * kSV};
+  float g[kSV], p[kSV], m[kSV], v[kSV];
+  // Unstaged, the state loads go first: with a compile-time row count every
+  // load of the tile is then in flight before the first add, and the run-time
+  // fold overlaps them with its first chunks.
+  constexpr bool state_last = staged_tile<OP, NG>();
+  if constexpr (OP != Op::Reduce && !state_last) {
+    loadf(a.p, at, p);
+    loadf(a.m, at, m);
+    loadf(a.v, at, v);
+  }
+  if constexpr (OP == Op::AdamW) {
+    loadf(a.grad, at, g);
+  } else {
+    if constexpr (NG == 0) {
+      if (a.bf16acc)
+        reduce_rows_general<kSV, true>(a.g, a.n_grads, a.group, a.s.gs, at, g);
+      else if (a.group < a.n_grads)
+        reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, at, g);
+      else
+        reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, at, g);
+    } else if constexpr (GRP > 0) {
+      reduce_rows_grouped<NG, GRP, BACC, state_last>(a.g, a.s.gs, at, g);
+    } else {
+      reduce_rows<NG, kSV, state_last>(a.g, a.n_grads, a.s.gs, at, g);
+    }
+  }
+  if constexpr (state_last) {
+    __builtin_amdgcn_sched_barrier(0);
+    loadf(a.p, at, p);
+    loadf(a.m, at, m);
+    loadf(a.v, at, v);
+  }
+  if constexpr (OP == Op::Reduce) {
+    out_f32(a.out, t0, tl, i, g);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
+    out_f32(a.p, t0, tl, i, p);
+    out_f32(a.m, t0, tl, i, m);
+    out_f32(a.v, t0, tl, i, v);
+    if constexpr (EMIT) out_bf16(a.w, t0, tl, i, p);
+  }
+}
+
 // Vector path: bf16 rows aligned to 2*kSV bytes, fp32 buffers to 16 bytes.
 // Lane t of a tile owns elements [tile + kSV*t, tile + kSV*t + kSV), so every
 // load and store instruction of a wavefront covers one contiguous range; the
@@ -536,45 +645,34 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
     if (i >= n) continue;
     if (i + kSV <= n) {
       const int64_t tl = n - t0 < tile ? n - t0 : tile;
-      const At at{t0, tl, uint32_t(threadIdx.x) * kSV};
-      float g[kSV], p[kSV], m[kSV], v[kSV];
-      // The state loads go first: with a compile-time row count every load of
-      // the tile is then in flight before the first add, and the run-time fold
-      // overlaps them with its first chunks.
-      if constexpr (OP != Op::Reduce) {
-        loadf(a.p, at, p);
-        loadf(a.m, at, m);
-        loadf(a.v, at, v);
-      }
-      if constexpr (OP == Op::AdamW) {
-        loadf(a.grad, at, g);
-      } else {
-        if constexpr (NG == 0) {
-          if (a.bf16acc)
-            reduce_rows_general<kSV, true>(a.g, a.n_grads, a.group, a.s.gs, at, g);
-          else if (a.group < a.n_grads)
-            reduce_rows_general<kSV, false>(a.g, a.n_grads, a.group, a.s.gs, at, g);
-          else
-            reduce_rows<0, kSV>(a.g, a.n_grads, a.s.gs, at, g);
-        } else if constexpr (GRP > 0) {
-          reduce_rows_grouped<NG, GRP, BACC>(a.g, a.s.gs, at, g);
-        } else {
-          reduce_rows<NG, kSV>(a.g, a.n_grads, a.s.gs, at, g);
-        }
-      }
-      if constexpr (OP == Op::Reduce) {
-        out_f32(a.out, t0, tl, i, g);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kSV; ++e) adamw(g[e], p[e], m[e], v[e], a.s);
-        out_f32(a.p, t0, tl, i, p);
-        out_f32(a.m, t0, tl, i, m);
-        out_f32(a.v, t0, tl, i, v);
-        if constexpr (EMIT) out_bf16(a.w, t0, tl, i, p);
-      }
+      step_tile<OP, NG, EMIT, GRP, BACC>(a, t0, tl, i);
     } else {
       for (int64_t j = i; j < n; ++j) step_scalar<OP>(a, j);
     }
+  }
+}
+
+// The vector path with one-wave workgroups and one tile each (grid = the tile
+// count, tiles in plain order), for the staged fused step. The kernel
+// arguments the first stage needs are fetched in one scalar round trip (the
+// general kernel's loop and XCD-run test cost a second one before the first
+// row load); that start-up latency is paid once per tile and, with staged
+// loads, showed up in the stream rate.
+template <int NG, bool EMIT, int GRP = 0, bool BACC = false>
+__global__ __launch_bounds__(kSmallThreads) void k_step_one(StepArgs a) {
+  constexpr int64_t tile = int64_t(kSmallThreads) * kSV;
+  const int64_t t0 = int64_t(blockIdx.x) * tile;
+  const int64_t i = t0 + int64_t(threadIdx.x) * kSV;
+  const int64_t n = a.n;
+  // empty uses that make the compiler fetch n and the row pointers together
+#pragma unroll
+  for (int k = 0; k < NG; ++k) asm volatile("" : : "s"(a.g[k]), "s"(n));
+  if (t0 + tile <= n) {
+    step_tile<Op::Fused, NG, EMIT, GRP, BACC>(a, t0, tile, i);
+  } else if (i + kSV <= n) {
+    step_tile<Op::Fused, NG, EMIT, GRP, BACC>(a, t0, n - t0, i);
+  } else {
+    for (int64_t j = i; j < n; ++j) step_scalar<Op::Fused>(a, j);
   }
 }
 
@@ -895,6 +993,11 @@ size_t lds_reservation(int wg_per_cu) {
 //    size: a CU's 1/256 share of 8 TB/s over a loaded latency of a few
 //    microseconds. The one-wave tiles keep each CU's write streams short and
 //    the end of a launch short;
+//  * the fused step with a compile-time fold of 8 or more rows stages its
+//    tile loads (step_tile) and runs FSDP_STAGED_WG_PER_CU (10) one-wave
+//    workgroups per CU, without XCD runs in k_step_one (9-11 measured alike
+//    for 8 and 16 rows; 8 and 12 were slower); with fewer rows a stage holds
+//    too few bytes and the unstaged tile keeps the lane-budget count;
 //  * the fused step with a run-time row count, folded flat, runs one-wave
 //    workgroups, FSDP_CHUNKED_WG_PER_CU per CU: a lane has one chunk of 8 rows
 //    in flight at a time, so it needs more waves than its bytes suggest (11
@@ -929,6 +1032,8 @@ int lane_bytes(const StepArgs& a) {
 template <Op OP>
 Shape step_shape(const StepArgs& a) {
   if (a.n < (int64_t(1) << FSDP_CAP_MIN_LOG2)) return Shape{kStepThreads, 0};
+  if (OP == Op::Fused && compile_time_fold(a) && a.n_grads >= 8)
+    return Shape{kSmallThreads, FSDP_STAGED_WG_PER_CU};   // staged tile loads (step_tile)
   if (OP == Op::AdamW || compile_time_fold(a)) {
     const int b = lane_bytes<OP>(a);
     const int wg = std::min(32, std::max(8, (FSDP_LANE_BUDGET + b / 2) / b));
@@ -973,6 +1078,32 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, size_t lds, hi
   }
   }
 }
+// The staged fused step in its one-tile kernel (one-wave workgroups, tiles in
+// plain order, grid = the tile count); false when the fold has no staged
+// instantiation.
+template <bool EMIT>
+bool launch_one(const StepArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
+  if (a.group < a.n_grads || a.bf16acc) {
+    if (!a.bf16acc && a.n_grads == 16 && a.group == 8)
+      k_step_one<16, EMIT, 8, false><<<grid, kSmallThreads, lds, stream>>>(a);
+    else if (!a.bf16acc && a.n_grads == 8 && a.group == 4)
+      k_step_one<8, EMIT, 4, false><<<grid, kSmallThreads, lds, stream>>>(a);
+    else if (a.bf16acc && a.n_grads == 16 && a.group == 16)
+      k_step_one<16, EMIT, 16, true><<<grid, kSmallThreads, lds, stream>>>(a);
+    else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
+      k_step_one<8, EMIT, 8, true><<<grid, kSmallThreads, lds, stream>>>(a);
+    else
+      return false;
+  } else if (a.n_grads == 8) {
+    k_step_one<8, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
+  } else if (a.n_grads == 16) {
+    k_step_one<16, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
+  } else {
+    return false;
+  }
+  return true;
+}
+
 template <Op OP, bool EMIT>
 void launch_shift_ng(const StepArgs& a, unsigned grid, int threads, size_t lds,
                      hipStream_t stream) {
@@ -1017,8 +1148,15 @@ fsdp_status launch_step(const StepArgs& args, Path path, hipStream_t stream, con
     const int64_t tile = int64_t(sh.threads) * kSV;
     const unsigned grid = grid_for((a.n + tile - 1) / tile);
     const size_t lds = lds_reservation(sh.wg_per_cu);
-    if (a.w) launch_vec_ng<OP, true>(a, grid, sh.threads, lds, stream);
-    else launch_vec_ng<OP, false>(a, grid, sh.threads, lds, stream);
+    bool done = false;
+    if constexpr (OP == Op::Fused) {
+      if (sh.threads == kSmallThreads && !a.runs)   // grid * tile covers n: one tile each
+        done = a.w ? launch_one<true>(a, grid, lds, stream) : launch_one<false>(a, grid, lds, stream);
+    }
+    if (!done) {
+      if (a.w) launch_vec_ng<OP, true>(a, grid, sh.threads, lds, stream);
+      else launch_vec_ng<OP, false>(a, grid, sh.threads, lds, stream);
+    }
   } else if (path == Path::Shifted) {
     if constexpr (OP != Op::AdamW) {
       // the same occupancy plan as the vector path (the shifted path only folds flat)

@@ -133,7 +133,7 @@ def test_traffic_summary_from_raw_request_counts(tmp_path, capsys):
     """Bytes from 128-byte read and 64-byte write requests; the two 1 GiB copies of known
     size gate the result, and a copy whose counts do not match its size stops it."""
     U, S = 202383360, 25297920
-    fused = "void (anonymous namespace)::k_step_vec<((anonymous namespace)::Op)2, 8, true, 0, false>(x)"
+    fused = "void (anonymous namespace)::k_step_one<8, true, 0, false>((anonymous namespace)::StepArgs)"
     gather = "void (anonymous namespace)::k_segcopy<1>((anonymous namespace)::SegArgs)"
     lcopy = "void (anonymous namespace)::k_segcopy<0>((anonymous namespace)::SegArgs)"
     rcopy = "__amd_rocclr_copyBuffer"
