@@ -576,9 +576,11 @@ __device__ __forceinline__ int64_t shift_tile(unsigned b, unsigned nb) {
 // MI355X with rotating buffer sets, a wave that issues its 8 or 16 rows and
 // its state at once (64-80% of a tile's loads in one burst) kept the stream
 // mix 1-2% below a wave that keeps at most 8 rows' or the state's loads in
-// flight, with 10 rather than 8 one-wave workgroups per CU.
+// flight, with 10 rather than 8 one-wave workgroups per CU. The run-time fold
+// (chunks of 8 already) takes its state last too: 0-1.3% faster for 11 and 13
+// rows, 1-5% for 64. With 1-7 rows a stage is too small to stand alone.
 template <Op OP, int NG>
-constexpr bool staged_tile() { return OP == Op::Fused && NG >= 8; }
+constexpr bool staged_tile() { return OP == Op::Fused && (NG >= 8 || NG == 0); }
 
 // One workgroup tile of the vector path: elements [t0, t0 + tl), lane element i.
 template <Op OP, int NG, bool EMIT, int GRP, bool BACC>
@@ -653,7 +655,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
 }
 
 // The vector path with one-wave workgroups and one tile each (grid = the tile
-// count, tiles in plain order), for the staged fused step. The kernel
+// count, tiles in plain order), for the staged fused step (8 or 16 rows, the
+// grouped folds of those counts, and the flat run-time fold). The kernel
 // arguments the first stage needs are fetched in one scalar round trip (the
 // general kernel's loop and XCD-run test cost a second one before the first
 // row load); that start-up latency is paid once per tile and, with staged
@@ -1002,7 +1005,9 @@ size_t lds_reservation(int wg_per_cu) {
 //    workgroups, FSDP_CHUNKED_WG_PER_CU per CU: a lane has one chunk of 8 rows
 //    in flight at a time, so it needs more waves than its bytes suggest (11
 //    and 13 rows: best at 12 out of 6 to 24; 2-7% faster than 256-thread
-//    workgroups at rank 0, -1 to +3% at the last rank);
+//    workgroups at rank 0, -1 to +3% at the last rank; with the state loads
+//    last, 12 stayed best out of 10, 12 and 16), in k_step_one without XCD
+//    runs;
 //  * the reduce with a run-time row count, and the grouped folds of a
 //    run-time count, are not capped (256 threads): one-wave workgroups made
 //    that reduce 3-20% slower.
@@ -1079,8 +1084,8 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, size_t lds, hi
   }
 }
 // The staged fused step in its one-tile kernel (one-wave workgroups, tiles in
-// plain order, grid = the tile count); false when the fold has no staged
-// instantiation.
+// plain order, grid = the tile count); false when the fold has no one-tile
+// instantiation (1-7 rows, the grouped folds of run-time counts).
 template <bool EMIT>
 bool launch_one(const StepArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
   if (a.group < a.n_grads || a.bf16acc) {
@@ -1098,6 +1103,8 @@ bool launch_one(const StepArgs& a, unsigned grid, size_t lds, hipStream_t stream
     k_step_one<8, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
   } else if (a.n_grads == 16) {
     k_step_one<16, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
+  } else if (!compile_time_fold(a)) {
+    k_step_one<0, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);   // run-time count, flat
   } else {
     return false;
   }
