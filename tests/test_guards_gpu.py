@@ -150,33 +150,46 @@ def test_grouped_fold_guards(lib, kind):
 
 
 LONG_GUARD_CASES = [
-    # name, F, S, rank: 8 rows over 2^24 + 3 elements (a ragged last tile) in one-wave
-    # workgroups, with aligned gradient windows (rank 0) and windows at a 6-byte offset
-    # (rank 1: the shifted-row path); 11 and 64 rows folded in chunks of 8 at run time
-    # (the 11-row fold ends in a partial chunk), over 2^23 + 5 and 2^22 + 7 elements
-    ("vector_rows", 8, (1 << 24) + 3, 0),
-    ("shifted_rows", 8, (1 << 24) + 3, 1),
-    ("chunked_rows11", 11, (1 << 23) + 5, 0),
-    ("chunked_rows64", 64, (1 << 22) + 7, 0),
+    # name, F, S, rank, row stride: 8 rows over 2^24 + 3 elements (a ragged last tile) in
+    # one-wave workgroups, with every row's window on a 128-byte line (rank 0, rows a
+    # multiple of 64 elements apart: the one-tile kernel of the staged step) and at a
+    # 6-byte offset (rank 1: the shifted-row path); 11 rows folded in chunks of 8 at run
+    # time over 2^23 + 5 elements (ending in a partial chunk), with the rows on lines and
+    # packed S elements apart (windows 2 bytes off: the shifted path); 64 rows over
+    # 2^22 + 7 elements
+    ("vector_rows", 8, (1 << 24) + 3, 0, "lines"),
+    ("shifted_rows", 8, (1 << 24) + 3, 1, "lines"),
+    ("chunked_rows11", 11, (1 << 23) + 5, 0, "lines"),
+    ("chunked_rows11_packed", 11, (1 << 23) + 5, 0, "packed"),
+    ("chunked_rows64", 64, (1 << 22) + 7, 0, "lines"),
+    ("chunked_rows64_packed", 64, (1 << 22) + 7, 0, "packed"),
 ]
 
 
-@pytest.mark.parametrize("name,F,S,rank", LONG_GUARD_CASES, ids=[c[0] for c in LONG_GUARD_CASES])
-def test_long_launch_guards(lib, name, F, S, rank):
+@pytest.mark.parametrize("name,F,S,rank,stride", LONG_GUARD_CASES,
+                         ids=[c[0] for c in LONG_GUARD_CASES])
+def test_long_launch_guards(lib, name, F, S, rank, stride):
     """Long launches, fused and reduce: the guards around the windows and the
     elements at both ends. Row k is the U-element view of one arena that starts at
-    element k*S (disjoint rank windows)."""
+    element k*Sr (disjoint rank windows), Sr = S ("packed") or S rounded up to a
+    multiple of 64 ("lines")."""
     u = lib.Unit([(F * S,)], F, rank)
     n = u.shard_valid
-    assert n == S and ((2 * u.shard_begin) % 8 == 0) == (name != "shifted_rows")
-    arena = torch.zeros((F - 1) * S + u.U, dtype=torch.bfloat16, device="cuda")
+    Sr = S if stride == "packed" else -(-S // 64) * 64
+    arena = torch.zeros((F - 1) * Sr + u.U, dtype=torch.bfloat16, device="cuda")
     rows = []
     for k in range(F):
-        r = arena[k * S:k * S + u.U]
+        r = arena[k * Sr:k * Sr + u.U]
         datagen.fill_bf16_(r[u.shard_begin:u.shard_begin + n], 5, k, 1e-3, start=u.shard_begin)
         rows.append(r)
-    p, m, v = state_for(n)
-    w = Guarded(n, torch.bfloat16)
+    starts = [r.data_ptr() + 2 * u.shard_begin for r in rows]
+    assert n == S
+    if name == "shifted_rows" or stride == "packed":
+        assert any(a % 8 for a in starts)             # the shifted-row path
+    else:
+        assert all(a % 128 == 0 for a in starts)      # the vector path, tiles in plain order
+    p, m, v = state_for(n)                              # windows 384 bytes in: on a line
+    w = Guarded(n, torch.bfloat16, lead=128)            # 256 bytes in: on a line
     lib.reduce_adamw_shard(u, rows, p.win, m.win, v.win, w.win, hp(lib), 1)
     out = Guarded(n, torch.float32)
     lib.reduce_shard(u, rows, out.win)

@@ -728,6 +728,72 @@ def test_xcd_runs_cover_every_element(offset, fused):
 
 
 # ---------------------------------------------------------------------------
+# the one-tile kernel of the staged fused step: every element, ragged end
+# ---------------------------------------------------------------------------
+
+ONE_TILE_CASES = [
+    # name, unit F, replicas, rows, bf16 partials, emit
+    ("flat8", 1, 1, 8, False, True),
+    ("flat8_no_emit", 1, 1, 8, False, False),
+    ("flat16", 1, 1, 16, False, True),
+    ("hybrid_2x4", 4, 2, 8, False, True),
+    ("bf16acc8", 1, 1, 8, True, True),
+    ("bf16acc16", 1, 1, 16, True, True),
+    ("runtime11", 1, 1, 11, False, True),
+]
+
+
+@pytest.mark.parametrize("name,F,R,ng,bacc,emit", ONE_TILE_CASES, ids=[c[0] for c in ONE_TILE_CASES])
+def test_one_tile_kernel_ragged_end_every_element(name, F, R, ng, bacc, emit):
+    """The staged fused step in its one-tile kernel (one-wave workgroups, every window
+    on a 128-byte line, 2^23 + 131 elements): the last tile holds 32 whole lanes and a
+    3-element scalar tail. Every element against the oracle, bit for bit, from a
+    non-zero optimizer state at step 3, with NaN guards after every output window."""
+    n = (1 << 23) + 131
+    u = fsdp.Unit([(F * n,)], F, 0)
+    L = O.unit_layout([(F * n,)], F, 0)
+    assert u.shard_valid == n and u.shard_begin == 0
+    seed = datagen.seed_for(47, 1, 1)
+    rows = [torch.empty(F * n, dtype=torch.bfloat16, device=DEV) for _ in range(ng)]
+    for k, r in enumerate(rows):                  # rank 0 reads [0, n) of each row
+        datagen.fill_bf16_(r[:n], seed, k, W.GRAD_SIGMA)
+    host = [to_np(r[:n]) for r in rows]
+    G = 64
+
+    def guarded(dtype, bits):
+        buf = torch.empty(n + G, dtype=dtype, device=DEV)
+        buf.view(torch.int32 if dtype == torch.float32 else torch.int16).fill_(bits)
+        return buf
+
+    pb, mb, vb = (guarded(torch.float32, FP32_SENTINEL) for _ in range(3))
+    sseed = datagen.seed_for(47, 0)
+    datagen.fill_normal_f32_(pb[:n], sseed, 0, W.MASTER_SIGMA)
+    datagen.fill_normal_f32_(mb[:n], sseed, 1, 1e-4)
+    datagen.fill_normal_f32_(vb[:n], sseed, 2, 1e-6)
+    vb[:n].abs_()
+    p0, m0, v0 = (to_np(b[:n]).copy() for b in (pb, mb, vb))
+    wb = guarded(torch.bfloat16, BF16_SENTINEL) if emit else None
+    w = wb[:n] if emit else None
+    if R > 1:
+        fsdp.reduce_adamw_shard_hybrid(u, R, rows, pb[:n], mb[:n], vb[:n], w, HPD, 3)
+        want = O.reduce_adamw_shard_hybrid(host, L, R, p0, m0, v0, HP, 3, emit_bf16=emit)
+    elif bacc:
+        fsdp.reduce_adamw_shard_bf16acc(u, rows, pb[:n], mb[:n], vb[:n], w, HPD, 3)
+        want = O.reduce_adamw_shard_bf16acc(host, L, p0, m0, v0, HP, 3, emit_bf16=emit)
+    else:
+        fsdp.reduce_adamw_shard(u, rows, pb[:n], mb[:n], vb[:n], w, HPD, 3)
+        want = O.reduce_adamw_shard(host, L, p0, m0, v0, HP, 3, emit_bf16=emit)
+    torch.cuda.synchronize()
+    outs = [(pb, "master", FP32_SENTINEL), (mb, "exp_avg", FP32_SENTINEL),
+            (vb, "exp_avg_sq", FP32_SENTINEL)] + ([(wb, "w", BF16_SENTINEL)] if emit else [])
+    for (buf, nm, sent), exp in zip(outs, want):
+        got = to_np(buf)
+        assert_bits(_bits(got[:n]), _bits(exp), f"{name} {nm}")
+        tail = got[n:].view(np.uint32) if got.dtype == np.float32 else got[n:]
+        assert (tail == sent).all(), f"{name} {nm}: guard after the window"
+
+
+# ---------------------------------------------------------------------------
 # hybrid sharding (HSDP): R replica groups of F ranks
 # ---------------------------------------------------------------------------
 

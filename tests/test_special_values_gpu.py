@@ -266,23 +266,28 @@ def test_unfused_special_values(lib, case):
 # ---------------------------------------------------------------------------
 
 LONG_CASES = [
-    # F, S, rank: 8 rows over the 7B block's shard at F = 8 (compile-time fold, one-wave
-    # workgroups); 11 rows and 64 rows, folded in chunks of 8 at run time (for 11 rows
-    # the last chunk is partial)
-    (8, 25297920, 3),
-    (11, (1 << 23) + 5, 4),
-    (64, (1 << 22) + 7, 5),
+    # F, S, rank, row stride: 8 rows over the 7B block's shard at F = 8 (the staged
+    # compile-time fold in one-wave workgroups, its one-tile kernel); 11 rows and 64 rows,
+    # folded in chunks of 8 at run time (for 11 rows the last chunk is partial), with the
+    # rows packed S elements apart (windows off 8 bytes: the shifted path) and, for 11
+    # rows, on 128-byte lines (the vector path's one-tile kernel, a ragged last tile)
+    (8, 25297920, 3, "packed"),
+    (11, (1 << 23) + 5, 4, "packed"),
+    (11, (1 << 23) + 5, 0, "lines"),
+    (64, (1 << 22) + 7, 5, "packed"),
 ]
 
 
-@pytest.mark.parametrize("F,S,rank", LONG_CASES, ids=[f"rows{c[0]}" for c in LONG_CASES])
-def test_fused_special_values_long_launch(lib, F, S, rank):
+@pytest.mark.parametrize("F,S,rank,stride", LONG_CASES,
+                         ids=[f"rows{c[0]}_{c[3]}" for c in LONG_CASES])
+def test_fused_special_values_long_launch(lib, F, S, rank, stride):
     """F rows over an S-element shard (rank `rank` of F): normal draws in HBM with
     specials planted at 2^17 random positions and in one contiguous run that spans
     several workgroup tiles; those positions and the run are compared with the
     oracle element by element. Row k is the U-element view of one arena that
-    starts at element k*S, so the rank windows of the rows are disjoint (the views
-    overlap outside them, where the step reads nothing)."""
+    starts at element k*Sr (Sr = S, or S rounded up to a multiple of 64), so the
+    rank windows of the rows are disjoint (the views overlap outside them, where
+    the step reads nothing)."""
     n_rows = F
     shapes = [(F * S,)]
     L = O.unit_layout(shapes, F, rank)
@@ -292,10 +297,11 @@ def test_fused_special_values_long_launch(lib, F, S, rank):
     run = np.arange(123456, 123456 + 3000, dtype=np.int64)
     pos = np.unique(np.concatenate([rng.integers(0, n, 1 << 17), run, [0, n - 1]]))
     gseed, mseed = datagen.seed_for(9, 1, 77), datagen.seed_for(9, 0, 77)
-    arena = torch.empty((n_rows - 1) * S + L.U, dtype=torch.bfloat16, device="cuda")
+    Sr = S if stride == "packed" else -(-S // 64) * 64
+    arena = torch.empty((n_rows - 1) * Sr + L.U, dtype=torch.bfloat16, device="cuda")
     rows_dev, rows_at = [], []
     for k in range(n_rows):
-        r = arena[k * S:k * S + L.U]          # window: arena[kS + begin, kS + begin + S)
+        r = arena[k * Sr:k * Sr + L.U]        # window: arena[kSr + begin, kSr + begin + S)
         datagen.fill_bf16_(r[L.shard_begin:L.shard_begin + n], gseed, k, 1e-3,
                            start=L.shard_begin)
         at = datagen.bf16_bits_host(gseed, k, L.shard_begin + pos, 1e-3)
