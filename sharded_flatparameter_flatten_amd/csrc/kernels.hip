@@ -1157,7 +1157,8 @@ fsdp_status launch_step(const StepArgs& args, Path path, hipStream_t stream, con
     const size_t lds = lds_reservation(sh.wg_per_cu);
     bool done = false;
     if constexpr (OP == Op::Fused) {
-      if (sh.threads == kSmallThreads && !a.runs)   // grid * tile covers n: one tile each
+      // grid * tile covers n (the grid's x size holds the tile count): one tile each
+      if (sh.threads == kSmallThreads && !a.runs && (a.n + tile - 1) / tile <= INT32_MAX)
         done = a.w ? launch_one<true>(a, grid, lds, stream) : launch_one<false>(a, grid, lds, stream);
     }
     if (!done) {
