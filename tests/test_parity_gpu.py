@@ -685,17 +685,19 @@ def test_shifted_rows_with_aligned_state(shift, ng, fused):
 # tiles visited in XCD runs: every element of a long launch, ragged
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("ng", [3, 8, 16])
 @pytest.mark.parametrize("offset", [12, 1], ids=["rows_off_line", "rows_shifted"])
 @pytest.mark.parametrize("fused", [False, True])
-def test_xcd_runs_cover_every_element(offset, fused):
-    """3 gradient rows whose windows start `offset` elements past a 128-byte line (12:
+def test_xcd_runs_cover_every_element(offset, fused, ng):
+    """ng gradient rows whose windows start `offset` elements past a 128-byte line (12:
     8-byte aligned, the vector path; 1: 2 bytes off, the shifted path), over
-    2^23 + 12345 elements: both paths visit their tiles in runs of 8 per XCD. The launch
-    has 32,817 one-wave tiles: 512 whole groups of 64 (8 runs of 8) and 49 tiles past them
-    in the plain order, the last one ragged. Every element against the oracle, bit for
-    bit."""
+    2^23 + 12345 elements: both paths visit their tiles in runs of 8 per XCD (with 8
+    and 16 rows the fused vector path stages its loads in the general kernel). The
+    launch has 32,817 one-wave tiles: 512 whole groups of 64 (8 runs of 8) and 49 tiles
+    past them in the plain order, the last one ragged. Every element against the
+    oracle, bit for bit."""
     n = (1 << 23) + 12345
-    shapes, F, rank, ng = [(n,)], 1, 0, 3
+    shapes, F, rank = [(n,)], 1, 0
     u = fsdp.Unit(shapes, F, rank)
     L = O.unit_layout(shapes, F, rank)
     seed = datagen.seed_for(46, 1, 1)
