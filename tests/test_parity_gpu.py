@@ -924,17 +924,31 @@ def test_bf16acc_blk7_every_rank_every_element():
 
 
 @pytest.mark.parametrize("n_grads", [8, 11, 24])
-def test_unfused_long_launch_sampled(n_grads):
+def test_unfused_long_launch(n_grads):
     """fsdp_reduce_shard then fsdp_adamw_shard on a 202,383,360-element shard (the 7B
     block at F=1): 8 gradient rows (a compile-time fold in one-wave workgroups, 16
     per CU for this reduce, 11 for the AdamW), 11 and 24 rows (a run-time count
-    folded in chunks of 8; the 11-row fold ends in a partial chunk); sampled indices
-    against the oracle, two steps."""
+    folded in chunks of 8; the 11-row fold ends in a partial chunk); two steps. Every
+    element of the reduced gradient and of the state after each step against the
+    oracle on host copies of the device fills (spot-checked against the host
+    generator), and sampled indices against host-regenerated inputs."""
     case = Case(W.shapes(W.BLK7), 1, 0, n_grads=n_grads, config=44)
     u = fsdp.Unit(case.shapes, 1, 0)
-    assert u.shard_valid >= 1 << 25
+    L = case.L
+    n = u.shard_valid
+    assert n >= 1 << 25
+    masters = case.device_master_tensors()
+    spot = case.sample_indices(4096, seed=n_grads)
+    torch.cuda.synchronize()
+    host_m = [to_np(t) for t in masters]
+    assert_bits(np.concatenate(host_m)[spot].view(np.uint32),
+                case.host_master_at(spot).view(np.uint32), "master fill")
+    hp = O.flatten_pad([t.view(np.uint32) for t in host_m], 1).view(np.float32)[:n].copy()
+    hm, hv = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    del host_m
     p = torch.empty(u.S, dtype=torch.float32, device=DEV)
-    fsdp.flatten_pad(u, case.device_master_tensors(), p)
+    fsdp.flatten_pad(u, masters, p)
+    del masters
     m, v = torch.zeros_like(p), torch.zeros_like(p)
     w = torch.empty(u.S, dtype=torch.bfloat16, device=DEV)
     g32 = torch.empty(u.S, dtype=torch.float32, device=DEV)
@@ -943,6 +957,19 @@ def test_unfused_long_launch_sampled(n_grads):
         grads = case.device_grads(t, out=grads)
         fsdp.reduce_shard(u, grads, g32)
         fsdp.adamw_shard(u, g32, p, m, v, w, HPD, t)
+        torch.cuda.synchronize()
+        rows = [to_np(g) for g in grads]
+        want_rows = case.host_grads_at(t, spot)
+        for k in (0, n_grads - 1):
+            assert_bits(rows[k][spot], want_rows[k], f"step {t} row {k} fill")
+        gw = O.reduce_shard(rows, L)
+        del rows
+        assert_bits(to_np(g32)[:n].view(np.uint32), gw.view(np.uint32), f"step {t} reduced gradient")
+        want = O.adamw_step(gw, hp, hm, hv, HP, t, True)
+        hp, hm, hv = want[:3]
+        for got, exp, name in zip((p, m, v, w), want, ("master", "exp_avg", "exp_avg_sq", "w")):
+            assert_bits(_bits(to_np(got)[:n]), _bits(exp), f"unfused F=1 {n_grads} rows step {t} {name}")
+        log(f"{n_grads} rows step {t}: every element of {n:,} bit-equal")
     torch.cuda.synchronize()
     loc = case.sample_indices()
     want = case.oracle_sampled(loc, 2)[-1]
