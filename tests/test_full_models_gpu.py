@@ -5,10 +5,11 @@
 * Llama-70B-shaped rank shard: 80 GQA block units + root, F=8, rank 0,
   ~8.62B params (~138 GB of persistent state resident in HBM).
 One fused reduce + AdamW + bf16 step per unit on one stream. Every element of
-the named units and of the root unit is checked against the oracle (run on
-host copies of the generator's device fills, which are spot-checked against
-its host form first), and sampled indices of every other unit (with the
-oracle's inputs regenerated on the host). Persistent bytes allocated equal
+the named units and of the root unit (for the 7B shard through the per-unit
+calls: of every unit) is checked against the oracle (run on host copies of
+the generator's device fills, which are spot-checked against its host form
+first), and sampled indices of every unit (with the oracle's inputs
+regenerated on the host). Persistent bytes allocated equal
 16 * sum(S) per the pages' budget.
 """
 
@@ -33,14 +34,19 @@ import sharded_flatparameter_flatten_amd as fsdp  # noqa: E402
 HPD = fsdp.AdamWHparams(**W.ADAMW)
 
 
-def check_every_element(ms, i, p_before, what):
+def check_every_element(ms, i, p_before, what, row_cache):
     """Unit i's window after the step against the oracle on every element. The
     oracle's inputs are host copies of the device fills (the rank window of
     each gradient row and the master before the step), each spot-checked
-    against the host generator."""
+    against the host generator. row_cache keeps the host copies of rows that
+    several units share."""
     L = ms.L[i]
     lo, n = L.shard_begin, L.shard_valid
-    rows = [to_np(g[lo:lo + n]) for g in ms.grads(i)]
+    key = (id(ms.grads(i)), lo, n)
+    if key not in row_cache:
+        row_cache.clear()
+        row_cache[key] = [to_np(g[lo:lo + n]) for g in ms.grads(i)]
+    rows = row_cache[key]
     loc = ms.sample(i, 4096, seed=1000 + i)
     want_in = ms.inputs_at(i, loc)
     for k in (0, ms.F - 1):
@@ -73,10 +79,11 @@ def run_model(name, full_units, sparse_n, multi=False):
             fsdp.reduce_adamw_shard(u, ms.grads(i), ms.window(ms.p, i), ms.window(ms.m, i),
                                     ms.window(ms.v, i), ms.window(ms.w, i), HPD, 1)
     torch.cuda.synchronize()
+    row_cache = {}
     for i in range(n_units):
         what = f"{name} unit {i}"
         if i in full_units:
-            check_every_element(ms, i, p_before.pop(i), what)
+            check_every_element(ms, i, p_before.pop(i), what, row_cache)
             print(f"{what}: every element of {units[i].shard_valid:,} checked", flush=True)
         loc = ms.sample(i, sparse_n, seed=i)
         want = ms.oracle_sampled(i, loc)
@@ -96,7 +103,10 @@ def run_model(name, full_units, sparse_n, multi=False):
 
 @pytest.mark.parametrize("multi", [False, True])
 def test_full_7b_rank_shard_every_unit(multi):
-    assert run_model("full7b", {0, 15, 31}, 4096, multi) == 13_476_831_232
+    """Per-unit calls: every element of every unit (842M shard elements); the batched
+    entry point: every element of the named units, sampled indices of the rest."""
+    full = set(range(33)) if not multi else {0, 15, 31}
+    assert run_model("full7b", full, 4096, multi) == 13_476_831_232
 
 
 def test_full_70b_rank_shard_every_unit():
