@@ -799,7 +799,7 @@ def test_one_tile_kernel_ragged_end_every_element(name, F, R, ng, bacc, emit):
 # hybrid sharding (HSDP): R replica groups of F ranks
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,F", [(2, 2), (2, 4), (3, 4), (2, 8), (4, 8)])
+@pytest.mark.parametrize("R,F", [(2, 2), (2, 4), (3, 4), (2, 8), (4, 8), (8, 8)])   # 8 x 8: 64 rows
 def test_hybrid_fused_every_rank_every_element(R, F):
     shapes = [(1000, 7), (33,)]
     for rank in range(F):
@@ -884,7 +884,8 @@ def test_hybrid_blk7_two_groups_of_8_every_rank_every_element():
 
 @pytest.mark.parametrize("shapes,F,ng", [([(1000, 7), (33,)], 4, 4), ([(1000, 7), (33,)], 8, 8),
                                          ([(5000,)], 4, 12), ([(1000, 3), (17,)], 7, 7),
-                                         ([(1000, 7), (33,)], 8, 16)])
+                                         ([(1000, 7), (33,)], 8, 16),
+                                         ([(1000, 7), (33,)], 8, 64)])     # the row limit
 def test_bf16acc_fused_every_rank_every_element(shapes, F, ng):
     for rank in range(F):
         case = Case(shapes, F, rank, n_grads=ng, config=40, outliers=True, bf16acc=True)
