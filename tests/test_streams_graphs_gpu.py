@@ -129,11 +129,15 @@ def test_graph_captured_step_replays_like_eager():
 
 def test_graph_captured_capped_launches_replay_like_eager():
     """Launches long enough to run with the occupancy cap (at least 8192 workgroups:
-    one 9M-element unit through the single-unit fused kernel, and 30 units of 300K
-    through the batched kernel) captured into a graph: every replay equals eager."""
-    big = Case([(4096, 2200)], 1, 0, config=15)             # 8800 tiles
+    9M-element units through the single-unit fused kernels, with 1 row, with 8 rows
+    (the staged one-tile kernel) and with 11 rows (the run-time fold in it), and 30
+    units of 300K through the batched kernel) captured into a graph: every replay
+    equals eager."""
+    bigs = [Case([(4096, 2200)], 1, 0, n_grads=ng, config=15 + 40 * j)   # 8800 tiles each
+            for j, ng in enumerate((1, 8, 11))]
     mids = [Case([(600, 500)], 1, 0, config=16 + j) for j in range(30)]   # 30 x 293 tiles
-    cases = [big] + mids
+    cases = bigs + mids
+    nb = len(bigs)
     units = [fsdp.Unit(c.shapes, c.F, c.rank) for c in cases]
     grads = [c.device_grads(1) for c in cases]
     start = [_state(c)[1:4] for c in cases]
@@ -144,9 +148,10 @@ def test_graph_captured_capped_launches_replay_like_eager():
                 for s, u in zip(start, units)]
 
     def step(st):
-        u0, (p, m, v, w) = units[0], st[0]
-        fsdp.reduce_adamw_shard(u0, grads[0], p, m, v, w, HPD, 3)
-        fsdp.reduce_adamw_units([(u, g) + tuple(s) for u, g, s in zip(units[1:], grads[1:], st[1:])],
+        for j in range(nb):
+            p, m, v, w = st[j]
+            fsdp.reduce_adamw_shard(units[j], grads[j], p, m, v, w, HPD, 3)
+        fsdp.reduce_adamw_units([(u, g) + tuple(s) for u, g, s in zip(units[nb:], grads[nb:], st[nb:])],
                                 HPD, 3)
 
     eager_st = state_copy()
