@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step_vec(StepArgs a) {
 
 // The vector path with one-wave workgroups and one tile each (grid = the tile
 // count, tiles in plain order), for the staged fused step (8 or 16 rows, the
-// grouped folds of those counts, and the flat run-time fold). The kernel
+// compile-time grouped folds, and the flat run-time fold). The kernel
 // arguments the first stage needs are fetched in one scalar round trip (the
 // general kernel's loop and XCD-run test cost a second one before the first
 // row load); that start-up latency is paid once per tile and, with staged
@@ -1017,12 +1017,21 @@ struct Shape {
   int wg_per_cu;
 };
 
-bool compile_time_fold(const StepArgs& a) {
+// Hybrid sharding with 3 or 4 replica groups of 8 ranks: compile-time grouped
+// folds of the fused step only (its staged loads, 3 or 4 stages of one group
+// each: 4-6% faster than the run-time grouped fold on the 7B block); the reduce
+// folds them at run time.
+bool fused_wide_hybrid(const StepArgs& a) {
+  return !a.bf16acc && a.group == 8 && (a.n_grads == 24 || a.n_grads == 32);
+}
+
+bool compile_time_fold(const StepArgs& a, Op op) {
   if (a.group < a.n_grads || a.bf16acc)
     return (!a.bf16acc && a.n_grads == 16 && a.group == 8) ||
            (!a.bf16acc && a.n_grads == 8 && a.group == 4) ||
            (a.bf16acc && a.n_grads == 16 && a.group == 16) ||
-           (a.bf16acc && a.n_grads == 8 && a.group == 8);
+           (a.bf16acc && a.n_grads == 8 && a.group == 8) ||
+           (op == Op::Fused && fused_wide_hybrid(a));
   return (a.n_grads >= 1 && a.n_grads <= 8) || a.n_grads == 16;
 }
 
@@ -1038,9 +1047,9 @@ int lane_bytes(const StepArgs& a) {
 template <Op OP>
 Shape step_shape(const StepArgs& a) {
   if (a.n < (int64_t(1) << FSDP_CAP_MIN_LOG2)) return Shape{kStepThreads, 0};
-  if (OP == Op::Fused && compile_time_fold(a) && a.n_grads >= 8)
+  if (OP == Op::Fused && compile_time_fold(a, OP) && a.n_grads >= 8)
     return Shape{kSmallThreads, FSDP_STAGED_WG_PER_CU};   // staged tile loads (step_tile)
-  if (OP == Op::AdamW || compile_time_fold(a)) {
+  if (OP == Op::AdamW || compile_time_fold(a, OP)) {
     const int b = lane_bytes<OP>(a);
     const int wg = std::min(32, std::max(8, (FSDP_LANE_BUDGET + b / 2) / b));
     return Shape{kSmallThreads, wg};
@@ -1064,6 +1073,10 @@ void launch_vec_ng(const StepArgs& a, unsigned grid, int threads, size_t lds, hi
       k_step_vec<OP, 16, EMIT, 16, true><<<grid, threads, lds, stream>>>(a);
     else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
       k_step_vec<OP, 8, EMIT, 8, true><<<grid, threads, lds, stream>>>(a);
+    else if (OP == Op::Fused && fused_wide_hybrid(a) && a.n_grads == 24)
+      k_step_vec<Op::Fused, 24, EMIT, 8, false><<<grid, threads, lds, stream>>>(a);
+    else if (OP == Op::Fused && fused_wide_hybrid(a))
+      k_step_vec<Op::Fused, 32, EMIT, 8, false><<<grid, threads, lds, stream>>>(a);
     else
       k_step_vec<OP, 0, EMIT><<<grid, threads, lds, stream>>>(a);
   } else {
@@ -1098,13 +1111,17 @@ bool launch_one(const StepArgs& a, unsigned grid, size_t lds, hipStream_t stream
       k_step_one<16, EMIT, 16, true><<<grid, kSmallThreads, lds, stream>>>(a);
     else if (a.bf16acc && a.n_grads == 8 && a.group == 8)
       k_step_one<8, EMIT, 8, true><<<grid, kSmallThreads, lds, stream>>>(a);
+    else if (fused_wide_hybrid(a) && a.n_grads == 24)
+      k_step_one<24, EMIT, 8, false><<<grid, kSmallThreads, lds, stream>>>(a);
+    else if (fused_wide_hybrid(a))
+      k_step_one<32, EMIT, 8, false><<<grid, kSmallThreads, lds, stream>>>(a);
     else
       return false;
   } else if (a.n_grads == 8) {
     k_step_one<8, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
   } else if (a.n_grads == 16) {
     k_step_one<16, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);
-  } else if (!compile_time_fold(a)) {
+  } else if (!compile_time_fold(a, Op::Fused)) {
     k_step_one<0, EMIT><<<grid, kSmallThreads, lds, stream>>>(a);   // run-time count, flat
   } else {
     return false;

@@ -129,17 +129,18 @@ def test_reduce_and_adamw_guards(lib, case):
         t.check(f"{name} adamw {nm}")
 
 
-@pytest.mark.parametrize("kind", ["hybrid_2x4", "bf16acc_8", "bf16acc_6"])
+@pytest.mark.parametrize("kind", ["hybrid_2x4", "hybrid_3x8", "bf16acc_8", "bf16acc_6"])
 def test_grouped_fold_guards(lib, kind):
-    u = lib.Unit([(4 * 4100 - 2,)], 4, 3)
+    F, R = (8, 3) if kind == "hybrid_3x8" else (4, 2)
+    u = lib.Unit([(F * 4100 - 2,)], F, F - 1)
     n = u.shard_valid
-    rows = rows_for(u, 8 if kind != "bf16acc_6" else 6)
+    rows = rows_for(u, {"hybrid_2x4": 8, "hybrid_3x8": 24, "bf16acc_8": 8, "bf16acc_6": 6}[kind])
     p, m, v = state_for(n)
     w = Guarded(n, torch.bfloat16)
-    if kind == "hybrid_2x4":
-        lib.reduce_adamw_shard_hybrid(u, 2, rows, p.win, m.win, v.win, w.win, hp(lib), 1)
+    if kind.startswith("hybrid"):
+        lib.reduce_adamw_shard_hybrid(u, R, rows, p.win, m.win, v.win, w.win, hp(lib), 1)
         g = Guarded(n, torch.float32)
-        lib.reduce_shard_hybrid(u, 2, rows, g.win)
+        lib.reduce_shard_hybrid(u, R, rows, g.win)
     else:
         lib.reduce_adamw_shard_bf16acc(u, rows, p.win, m.win, v.win, w.win, hp(lib), 1)
         g = Guarded(n, torch.float32)

@@ -739,6 +739,8 @@ ONE_TILE_CASES = [
     ("flat8_no_emit", 1, 1, 8, False, False),
     ("flat16", 1, 1, 16, False, True),
     ("hybrid_2x4", 4, 2, 8, False, True),
+    ("hybrid_3x8", 8, 3, 24, False, True),
+    ("hybrid_4x8", 8, 4, 32, False, True),
     ("bf16acc8", 1, 1, 8, True, True),
     ("bf16acc16", 1, 1, 16, True, True),
     ("runtime11", 1, 1, 11, False, True),
@@ -799,7 +801,7 @@ def test_one_tile_kernel_ragged_end_every_element(name, F, R, ng, bacc, emit):
 # hybrid sharding (HSDP): R replica groups of F ranks
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,F", [(2, 2), (2, 4), (3, 4), (2, 8), (4, 8), (8, 8)])   # 8 x 8: 64 rows
+@pytest.mark.parametrize("R,F", [(2, 2), (2, 4), (3, 4), (2, 8), (3, 8), (4, 8), (8, 8)])   # 8 x 8: 64 rows
 def test_hybrid_fused_every_rank_every_element(R, F):
     shapes = [(1000, 7), (33,)]
     for rank in range(F):

@@ -176,6 +176,7 @@ CASES = [
     ("scalar_state", 4, 4100, 4 * 4100, 2, 4, 1, False, 1),
     ("runtime_rows_11", 4, 4100, 4 * 4100, 1, 11, 1, False, 0),
     ("hybrid_2x4", 4, 4100, 4 * 4100, 1, 8, 2, False, 0),
+    ("hybrid_3x8", 8, 2052, 8 * 2052, 5, 24, 3, False, 0),
     ("bf16acc_8", 8, 2052, 8 * 2052, 2, 8, 1, True, 0),
     ("bf16acc_runtime_5", 4, 4100, 4 * 4100, 1, 5, 1, True, 0),
 ]
