@@ -162,3 +162,15 @@ def test_traffic_summary_from_raw_request_counts(tmp_path, capsys):
     _counter_csv(tmp_path / "wr2", [(k, wr(w)) for k, _, w in bad])
     with pytest.raises(SystemExit):
         bench.pmc_summary(str(tmp_path / "rd2"), str(tmp_path / "wr2"))
+
+
+def test_fused_kernel_name_matching():
+    """The profile readers find the fused kernel by its demangled name: the one-tile
+    kernel of the staged step, or the general vector kernel, for the given row count."""
+    r8 = bench.fused_kernel_re(8)
+    assert r8.search("void (anonymous namespace)::k_step_one<8, true, 0, false>((anonymous namespace)::StepArgs)")
+    assert r8.search("void (anonymous namespace)::k_step_vec<((anonymous namespace)::Op)2, 8, true, 0, false>(x)")
+    assert not r8.search("void (anonymous namespace)::k_step_one<8, false, 0, false>(x)")      # no emission
+    assert not r8.search("void (anonymous namespace)::k_step_one<16, true, 8, false>(x)")      # hybrid 2 x 8
+    assert not r8.search("void (anonymous namespace)::k_step_vec<((anonymous namespace)::Op)0, 8, false, 0, false>(x)")
+    assert bench.fused_kernel_re(16).search("k_step_one<16, true, 0, false>")
